@@ -1,0 +1,123 @@
+/*
+ * fa355.h — C ABI of libfa355: exact, IO-aware softmax attention on MI355X (gfx950).
+ *
+ * What is computed (per batch entry b and head h):
+ *     S = scale * Q K^T            (Nq x Nk scores)
+ *     P = softmax(S) row by row    (causal: key j is visible to query i iff j <= i)
+ *     O = P V
+ *     LSE_i = m_i + ln(l_i)        (row maximum m_i of S and denominator l_i)
+ * The definition is "08 · FlashAttention", §一; the per-row log-sum-exp kept for
+ * the backward is "LLM Systems 22: Flash Attention", §3.2 (Backward:
+ * Recomputation).  The forward never writes S or P to device memory: it runs the
+ * online-softmax update of "08 · FlashAttention", §二 over key tiles held on chip.
+ * The backward recomputes P tile by tile from LSE (same §3.2) and returns
+ * dQ, dK, dV of L = sum(O * dO).
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers, allocated and owned by the caller.
+ *     The library allocates nothing, keeps no mutable global state and never
+ *     synchronises the device; all work is enqueued on `stream` (a hipStream_t,
+ *     NULL for the default stream) in stream order and returns immediately.
+ *   - q, k, v, o, dout, dq, dk, dv are bf16 (IEEE bfloat16), contiguous, with the
+ *     head dimension fastest:
+ *         dense   [B, N, H, d]   element (b, n, h, c) at ((b*N + n)*H + h)*d + c
+ *         packed  [total, H, d]  (varlen) row t = token t of the packed batch
+ *     These are the [total, num_heads, head_size] tensors of the mha_fwd entry
+ *     point in "Flash Attention 实现深度解析", §3.1.  Pointers must be 16-byte
+ *     aligned.
+ *   - lse is fp32: dense [B, H, Nq]; varlen [nseq, H, max_seqlen_q] (rows at or
+ *     past a sequence's length are not written).  Natural-log units of the
+ *     scaled scores.  4-byte aligned.
+ *   - d must be 64 or 128.  Causal dense calls need Nq == Nk.  Only the causal
+ *     mask is supported; no arbitrary masks ("08 · FlashAttention", §四 lists
+ *     these limits of the method's kernels and asks for an error, never a silent
+ *     fallback).
+ *   - Every call validates its arguments on the host before launching anything.
+ *     On a validation error nothing is enqueued or written and a negative
+ *     fa_status is returned.  A failed launch returns FA_ERR_LAUNCH.  Faults
+ *     inside a kernel surface at the caller's next synchronisation.
+ *   - Calls are reentrant and thread-safe (no shared mutable state).
+ */
+#ifndef FA355_H
+#define FA355_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum fa_status {
+    FA_OK = 0,
+    FA_ERR_NULL = -1,        /* a required pointer is NULL                         */
+    FA_ERR_SHAPE = -2,       /* a size is <= 0, or sizes are inconsistent/too big   */
+    FA_ERR_UNSUPPORTED = -3, /* d not in {64,128}, causal with Nq != Nk, bad scale  */
+    FA_ERR_ALIGN = -4,       /* a tensor pointer is not 16-byte (fp32: 4-byte) aligned */
+    FA_ERR_LAUNCH = -5,      /* the HIP runtime rejected a kernel launch            */
+    FA_ERR_WORKSPACE = -6    /* workspace missing or smaller than required          */
+} fa_status;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* fa_status_string(int status);
+
+/* Library version as 10000*major + 100*minor + patch. */
+int fa_version(void);
+
+/*
+ * Forward, dense batch.
+ *   q [B,Nq,H,d], k,v [B,Nk,H,d]  (read)      o [B,Nq,H,d] (written)
+ *   lse [B,H,Nq] fp32 (written)
+ *   scale: multiplies Q K^T (1/sqrt(d) for standard attention); must be finite and > 0.
+ *   causal: 0 or 1.
+ */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int B, int H, int Nq, int Nk, int d, float scale, int causal, void* stream);
+
+/*
+ * Forward, packed variable-length batch ("08 · FlashAttention", §四: packing
+ * with cu_seqlens instead of a padding mask).
+ *   cu_seqlens_q, cu_seqlens_k: int32 device arrays of nseq+1 prefix offsets,
+ *   starting at 0 and non-decreasing; sequence s owns rows [cu[s], cu[s+1]).
+ *   max_seqlen_q / max_seqlen_k bound every sequence length (precondition; with
+ *   the environment variable FA355_VALIDATE_CU_SEQLENS=1 the offsets are copied to
+ *   the host and checked, which synchronises the stream).
+ *   Causal varlen needs equal query and key lengths per sequence.
+ *   q [total_q,H,d], k,v [total_k,H,d], o [total_q,H,d], lse [nseq,H,max_seqlen_q].
+ */
+int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                  const int* cu_seqlens_q, const int* cu_seqlens_k, int nseq,
+                  int max_seqlen_q, int max_seqlen_k, int H, int d, float scale,
+                  int causal, void* stream);
+
+/*
+ * Bytes of device workspace fa_bwd / fa_bwd_varlen need: one fp32 value per
+ * query row and head (D_i = sum_c dO_ic * O_ic), laid out like lse.
+ * batch_or_nseq = B (dense) or nseq (varlen); nq = Nq (dense) or max_seqlen_q.
+ * Returns 0 for non-positive arguments.
+ */
+size_t fa_bwd_workspace_bytes(int batch_or_nseq, int H, int nq, int d);
+
+/*
+ * Backward, dense batch.  Inputs q, k, v, o, dout [B,N,H,d] and lse from the
+ * forward with the same arguments; outputs dq [B,Nq,H,d], dk, dv [B,Nk,H,d]
+ * (fully overwritten).  workspace: device buffer of at least
+ * fa_bwd_workspace_bytes(B,H,Nq,d) bytes, 4-byte aligned; its contents on entry
+ * do not matter and on return are unspecified.
+ */
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+           const float* lse, void* dq, void* dk, void* dv, void* workspace,
+           size_t workspace_bytes, int B, int H, int Nq, int Nk, int d, float scale,
+           int causal, void* stream);
+
+/* Backward, packed variable-length batch; arguments as fa_fwd_varlen and fa_bwd. */
+int fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o,
+                  const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                  void* workspace, size_t workspace_bytes, const int* cu_seqlens_q,
+                  const int* cu_seqlens_k, int nseq, int max_seqlen_q, int max_seqlen_k,
+                  int H, int d, float scale, int causal, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA355_H */

@@ -1,0 +1,282 @@
+// libfa355: C ABI (include/fa355.h) — host-side validation and kernel launch.
+//
+// Validation mirrors the eligibility limits of the method's kernels listed in
+// "08 · FlashAttention", §四 (bf16 only, head dim limited, contiguous tensors,
+// causal or no mask) and, as that section asks, refuses unsupported calls with an
+// explicit error instead of falling back silently.
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cmath>
+#include <cstdint>
+#include <cstdlib>
+#include <cstring>
+#include <vector>
+
+#include "../../include/fa355.h"
+#include "fa_bwd.hpp"
+#include "fa_fwd.hpp"
+
+using namespace fa355;
+
+namespace {
+
+constexpr int kVersion = 100;  // 0.1.0
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int check_common(int H, int d, float scale, int causal) {
+    if (H <= 0) return FA_ERR_SHAPE;
+    if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+    if (!(std::isfinite(scale) && scale > 0.f)) return FA_ERR_UNSUPPORTED;
+    if (causal != 0 && causal != 1) return FA_ERR_UNSUPPORTED;
+    return FA_OK;
+}
+
+// tokens * H * d elements must be addressable; grid sizes must fit an int.
+int check_sizes(int64_t tokens_q, int64_t tokens_k, int H, int d, int64_t grid) {
+    const int64_t lim = (int64_t)1 << 40;
+    if (tokens_q <= 0 || tokens_k <= 0) return FA_ERR_SHAPE;
+    if (tokens_q > INT_MAX || tokens_k > INT_MAX) return FA_ERR_SHAPE;
+    if (tokens_q * H * d > lim || tokens_k * H * d > lim) return FA_ERR_SHAPE;
+    if (grid <= 0 || grid > INT_MAX) return FA_ERR_SHAPE;
+    return FA_OK;
+}
+
+bool env_validate_cu() {
+    const char* e = std::getenv("FA355_VALIDATE_CU_SEQLENS");
+    return e && e[0] == '1';
+}
+
+// Debug-only check of cu_seqlens contents (copies to the host; synchronises).
+int validate_cu(const int* cu_q, const int* cu_k, int nseq, int max_q, int max_k, int causal,
+                hipStream_t s, int64_t* total_q, int64_t* total_k) {
+    std::vector<int> hq(nseq + 1), hk(nseq + 1);
+    if (hipMemcpyAsync(hq.data(), cu_q, sizeof(int) * (nseq + 1), hipMemcpyDeviceToHost, s) != hipSuccess ||
+        hipMemcpyAsync(hk.data(), cu_k, sizeof(int) * (nseq + 1), hipMemcpyDeviceToHost, s) != hipSuccess ||
+        hipStreamSynchronize(s) != hipSuccess)
+        return FA_ERR_LAUNCH;
+    if (hq[0] != 0 || hk[0] != 0) return FA_ERR_SHAPE;
+    for (int i = 0; i < nseq; ++i) {
+        const int lq = hq[i + 1] - hq[i], lk = hk[i + 1] - hk[i];
+        if (lq < 0 || lk < 0 || lq > max_q || lk > max_k) return FA_ERR_SHAPE;
+        if (causal && lq != lk) return FA_ERR_UNSUPPORTED;
+    }
+    *total_q = hq[nseq];
+    *total_k = hk[nseq];
+    return FA_OK;
+}
+
+template <typename K>
+int launch(K kernel, int grid, int block, hipStream_t s, const AttnParams& p) {
+    void* args[] = {const_cast<AttnParams*>(&p)};
+    hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(kernel), dim3(grid), dim3(block),
+                                   args, 0, s);
+    return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+template <int D, bool VARLEN>
+int launch_fwd_d(const AttnParams& p, int causal, hipStream_t s) {
+    const int grid = p.n_tiles * p.H * p.batch;
+    return causal ? launch(fa_fwd_kernel<D, true, VARLEN>, grid, 256, s, p)
+                  : launch(fa_fwd_kernel<D, false, VARLEN>, grid, 256, s, p);
+}
+
+template <bool VARLEN>
+int launch_fwd(const AttnParams& p, int d, int causal, hipStream_t s) {
+    return d == 64 ? launch_fwd_d<64, VARLEN>(p, causal, s) : launch_fwd_d<128, VARLEN>(p, causal, s);
+}
+
+template <int D, bool VARLEN>
+int launch_bwd_d(AttnParams p, int causal, hipStream_t s) {
+    using Pre = BwdPreCfg<D>;
+    using KV = BwdKVCfg<D>;
+    using Q = BwdQCfg<D>;
+    int st;
+    // 1) D_i = rowsum(dO * O)
+    {
+        AttnParams pp = p;
+        pp.n_tiles = (p.nq + Pre::ROWS - 1) / Pre::ROWS;
+        const int grid = pp.n_tiles * p.H * p.batch;
+        st = launch(fa_bwd_dot_kernel<D, VARLEN>, grid, Pre::THREADS, s, pp);
+        if (st) return st;
+    }
+    // 2) dK, dV: one work-group per key tile, no atomics
+    {
+        AttnParams pk = p;
+        pk.n_tiles = (p.nk + KV::BN - 1) / KV::BN;
+        const int grid = pk.n_tiles * p.H * p.batch;
+        st = causal ? launch(fa_bwd_dkdv_kernel<D, true, VARLEN>, grid, KV::NW * 64, s, pk)
+                    : launch(fa_bwd_dkdv_kernel<D, false, VARLEN>, grid, KV::NW * 64, s, pk);
+        if (st) return st;
+    }
+    // 3) dQ: one work-group per query tile, no atomics
+    {
+        AttnParams pq = p;
+        pq.n_tiles = (p.nq + Q::BM - 1) / Q::BM;
+        const int grid = pq.n_tiles * p.H * p.batch;
+        st = causal ? launch(fa_bwd_dq_kernel<D, true, VARLEN>, grid, Q::NW * 64, s, pq)
+                    : launch(fa_bwd_dq_kernel<D, false, VARLEN>, grid, Q::NW * 64, s, pq);
+    }
+    return st;
+}
+
+template <bool VARLEN>
+int launch_bwd(const AttnParams& p, int d, int causal, hipStream_t s) {
+    return d == 64 ? launch_bwd_d<64, VARLEN>(p, causal, s) : launch_bwd_d<128, VARLEN>(p, causal, s);
+}
+
+AttnParams base_params(const void* q, const void* k, const void* v, int batch, int H, int nq,
+                       int nk, float scale) {
+    AttnParams p;
+    std::memset(&p, 0, sizeof(p));
+    p.q = static_cast<const bf16*>(q);
+    p.k = static_cast<const bf16*>(k);
+    p.v = static_cast<const bf16*>(v);
+    p.batch = batch;
+    p.H = H;
+    p.nq = nq;
+    p.nk = nk;
+    p.scale = scale;
+    p.scale_log2 = scale * kLog2e;
+    return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fa_status_string(int status) {
+    switch (status) {
+        case FA_OK: return "FA_OK";
+        case FA_ERR_NULL: return "FA_ERR_NULL: a required pointer is NULL";
+        case FA_ERR_SHAPE: return "FA_ERR_SHAPE: a size is non-positive, inconsistent or too large";
+        case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: head dim must be 64 or 128, causal needs Nq == Nk, scale must be finite and positive";
+        case FA_ERR_ALIGN: return "FA_ERR_ALIGN: tensor pointers must be 16-byte aligned (fp32 buffers 4-byte)";
+        case FA_ERR_LAUNCH: return "FA_ERR_LAUNCH: the HIP runtime rejected a kernel launch";
+        case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace missing or too small";
+        default: return "FA_ERR_UNKNOWN";
+    }
+}
+
+int fa_version(void) { return kVersion; }
+
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq,
+           int Nk, int d, float scale, int causal, void* stream) {
+    if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+    if (B <= 0 || Nq <= 0 || Nk <= 0) return FA_ERR_SHAPE;
+    int st = check_common(H, d, scale, causal);
+    if (st) return st;
+    if (causal && Nq != Nk) return FA_ERR_UNSUPPORTED;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
+        return FA_ERR_ALIGN;
+    const int ntq = (Nq + 127) / 128;
+    st = check_sizes((int64_t)B * Nq, (int64_t)B * Nk, H, d, (int64_t)ntq * H * B);
+    if (st) return st;
+    AttnParams p = base_params(q, k, v, B, H, Nq, Nk, scale);
+    p.o = static_cast<bf16*>(o);
+    p.lse = lse;
+    p.n_tiles = ntq;
+    return launch_fwd<false>(p, d, causal, static_cast<hipStream_t>(stream));
+}
+
+int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                  const int* cu_seqlens_q, const int* cu_seqlens_k, int nseq, int max_seqlen_q,
+                  int max_seqlen_k, int H, int d, float scale, int causal, void* stream) {
+    if (!q || !k || !v || !o || !lse || !cu_seqlens_q || !cu_seqlens_k) return FA_ERR_NULL;
+    if (nseq <= 0 || max_seqlen_q <= 0 || max_seqlen_k <= 0) return FA_ERR_SHAPE;
+    int st = check_common(H, d, scale, causal);
+    if (st) return st;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4) ||
+        !aligned(cu_seqlens_q, 4) || !aligned(cu_seqlens_k, 4))
+        return FA_ERR_ALIGN;
+    const int ntq = (max_seqlen_q + 127) / 128;
+    st = check_sizes((int64_t)nseq * max_seqlen_q, (int64_t)nseq * max_seqlen_k, H, d,
+                     (int64_t)ntq * H * nseq);
+    if (st) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (env_validate_cu()) {
+        int64_t tq, tk;
+        st = validate_cu(cu_seqlens_q, cu_seqlens_k, nseq, max_seqlen_q, max_seqlen_k, causal, s, &tq, &tk);
+        if (st) return st;
+    }
+    AttnParams p = base_params(q, k, v, nseq, H, max_seqlen_q, max_seqlen_k, scale);
+    p.o = static_cast<bf16*>(o);
+    p.lse = lse;
+    p.cu_q = cu_seqlens_q;
+    p.cu_k = cu_seqlens_k;
+    p.n_tiles = ntq;
+    return launch_fwd<true>(p, d, causal, s);
+}
+
+size_t fa_bwd_workspace_bytes(int batch_or_nseq, int H, int nq, int d) {
+    (void)d;
+    if (batch_or_nseq <= 0 || H <= 0 || nq <= 0) return 0;
+    return sizeof(float) * (size_t)batch_or_nseq * (size_t)H * (size_t)nq;
+}
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+           const float* lse, void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+           int B, int H, int Nq, int Nk, int d, float scale, int causal, void* stream) {
+    if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return FA_ERR_NULL;
+    if (B <= 0 || Nq <= 0 || Nk <= 0) return FA_ERR_SHAPE;
+    int st = check_common(H, d, scale, causal);
+    if (st) return st;
+    if (causal && Nq != Nk) return FA_ERR_UNSUPPORTED;
+    if (!workspace || workspace_bytes < fa_bwd_workspace_bytes(B, H, Nq, d)) return FA_ERR_WORKSPACE;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(dout, 16) ||
+        !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(lse, 4) ||
+        !aligned(workspace, 4))
+        return FA_ERR_ALIGN;
+    st = check_sizes((int64_t)B * Nq, (int64_t)B * Nk, H, d, (int64_t)((Nq + 15) / 16) * H * B);
+    if (st) return st;
+    AttnParams p = base_params(q, k, v, B, H, Nq, Nk, scale);
+    p.o_in = static_cast<const bf16*>(o);
+    p.dout = static_cast<const bf16*>(dout);
+    p.lse_in = lse;
+    p.dq = static_cast<bf16*>(dq);
+    p.dk = static_cast<bf16*>(dk);
+    p.dv = static_cast<bf16*>(dv);
+    p.dvec = static_cast<float*>(workspace);
+    return launch_bwd<false>(p, d, causal, static_cast<hipStream_t>(stream));
+}
+
+int fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                  const float* lse, void* dq, void* dk, void* dv, void* workspace,
+                  size_t workspace_bytes, const int* cu_seqlens_q, const int* cu_seqlens_k, int nseq,
+                  int max_seqlen_q, int max_seqlen_k, int H, int d, float scale, int causal,
+                  void* stream) {
+    if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !cu_seqlens_q || !cu_seqlens_k)
+        return FA_ERR_NULL;
+    if (nseq <= 0 || max_seqlen_q <= 0 || max_seqlen_k <= 0) return FA_ERR_SHAPE;
+    int st = check_common(H, d, scale, causal);
+    if (st) return st;
+    if (!workspace || workspace_bytes < fa_bwd_workspace_bytes(nseq, H, max_seqlen_q, d))
+        return FA_ERR_WORKSPACE;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(dout, 16) ||
+        !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(lse, 4) ||
+        !aligned(workspace, 4) || !aligned(cu_seqlens_q, 4) || !aligned(cu_seqlens_k, 4))
+        return FA_ERR_ALIGN;
+    st = check_sizes((int64_t)nseq * max_seqlen_q, (int64_t)nseq * max_seqlen_k, H, d,
+                     (int64_t)((max_seqlen_q + 15) / 16) * H * nseq);
+    if (st) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (env_validate_cu()) {
+        int64_t tq, tk;
+        st = validate_cu(cu_seqlens_q, cu_seqlens_k, nseq, max_seqlen_q, max_seqlen_k, causal, s, &tq, &tk);
+        if (st) return st;
+    }
+    AttnParams p = base_params(q, k, v, nseq, H, max_seqlen_q, max_seqlen_k, scale);
+    p.o_in = static_cast<const bf16*>(o);
+    p.dout = static_cast<const bf16*>(dout);
+    p.lse_in = lse;
+    p.dq = static_cast<bf16*>(dq);
+    p.dk = static_cast<bf16*>(dk);
+    p.dv = static_cast<bf16*>(dv);
+    p.dvec = static_cast<float*>(workspace);
+    p.cu_q = cu_seqlens_q;
+    p.cu_k = cu_seqlens_k;
+    return launch_bwd<true>(p, d, causal, s);
+}
+
+}  // extern "C"

@@ -1,0 +1,398 @@
+// Backward kernels: dQ, dK, dV of L = sum(O * dO), recomputing P tile by tile.
+//
+// Method ("LLM Systems 22: Flash Attention", §3.2 Backward: Recomputation;
+// "08 · FlashAttention", §三): only the per-row LSE is kept from the forward; P is
+// recomputed on chip as exp(scale * Q K^T - LSE) for each (query tile, key tile)
+// pair.  With D_i = sum_c dO_ic O_ic the chain rule of the definition gives
+//     dV = P^T dO,   dP = dO V^T,   dS = P * (dP - D),
+//     dQ = scale * dS K,   dK = scale * dS^T Q.
+//
+// Three kernels, all stream-ordered and free of atomics (every output element
+// is owned by exactly one work-group, so results are bitwise deterministic):
+//   1. fa_bwd_dot_kernel:  D_i = rowsum(dO * O), one pass over O and dO.
+//   2. fa_bwd_dkdv_kernel: key-tile outer.  A work-group keeps a 128-key tile of
+//      K and V in registers (32 keys per wave) and the dK^T, dV^T accumulators on
+//      chip, streams the query tiles that can see those keys (Q, dO, LSE, D;
+//      double-buffered through LDS) and evaluates S, dP (row-wise LDS operand
+//      reads) and dV^T += dO^T P, dK^T += Q^T dS (transposed LDS operand reads).
+//      S = Q K^T is computed with keys as the accumulator's columns, so each
+//      lane's P / dS registers are directly the B operand of those products.
+//   3. fa_bwd_dq_kernel: query-tile outer, the forward's structure: Q and dO rows
+//      stay in registers, K and V tiles stream through LDS, and
+//      dQ^T += K^T dS^T uses S^T = K Q^T so dS feeds the product unchanged.
+// The dQ pass recomputes S and dP (two extra products) instead of
+// accumulating dQ across key tiles with atomics.
+#pragma once
+
+#include "fa_tiles.hpp"
+
+namespace fa355 {
+
+template <int D>
+struct BwdPreCfg {
+    static constexpr int THREADS = 256;
+    static constexpr int TPR = D / 8;             // threads per (row, head): 16 bytes each
+    static constexpr int ROWS = THREADS / TPR;
+};
+
+template <int D>
+struct BwdKVCfg {
+    static constexpr int NW = 4;
+    static constexpr int BN = 32 * NW;            // keys per work-group (32 per wave)
+    static constexpr int BMQ = 64;                // query rows per streamed stage
+    static constexpr int ROW_BYTES = D * 2;
+    static constexpr int TILE_BYTES = BMQ * ROW_BYTES;
+    static constexpr int STAT_BYTES = 2 * BMQ * 4;   // LSE then D, fp32
+    static constexpr int STAGE_BYTES = 2 * TILE_BYTES + STAT_BYTES;
+    static constexpr int LDS_BYTES = 2 * STAGE_BYTES;
+    static constexpr int KSTEPS = D / 16;
+    static constexpr int DBLK = D / 32;
+};
+
+template <int D>
+struct BwdQCfg {
+    static constexpr int NW = 4;
+    static constexpr int BM = 32 * NW;            // query rows per work-group
+    static constexpr int BN = 64;                 // key rows per tile
+    static constexpr int ROW_BYTES = D * 2;
+    static constexpr int TILE_BYTES = BN * ROW_BYTES;
+    static constexpr int LDS_BYTES = 2 * 2 * TILE_BYTES;
+    static constexpr int KSTEPS = D / 16;
+    static constexpr int DBLK = D / 32;
+    static constexpr int KB = BN / 32;
+};
+
+// ---------------------------------------------------------------------------
+// 1. D_i = sum_c dO_ic * O_ic  (fp32, laid out like LSE)
+template <int D, bool VARLEN>
+__global__ __launch_bounds__(256) void fa_bwd_dot_kernel(AttnParams p) {
+    using C = BwdPreCfg<D>;
+    const int tile = blockIdx.x % p.n_tiles;
+    const int bh = blockIdx.x / p.n_tiles;
+    const int h = bh % p.H;
+    const int b = bh / p.H;
+    int qs, nq, ks, nk;
+    seq_range<VARLEN>(p, b, qs, nq, ks, nk);
+    const int r = tile * C::ROWS + (int)threadIdx.x / C::TPR;
+    const int c8 = (int)threadIdx.x % C::TPR;
+    float acc = 0.f;
+    if (r < nq) {
+        const int64_t off = (int64_t)(qs + r) * p.H * D + h * D + 8 * c8;
+        const bf16x8 o = load16(p.o_in + off);
+        const bf16x8 g = load16(p.dout + off);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc = __builtin_fmaf((float)o[e], (float)g[e], acc);
+    }
+#pragma unroll
+    for (int w = C::TPR / 2; w > 0; w >>= 1) acc += __shfl_xor(acc, w);
+    if (c8 == 0 && r < nq) p.dvec[((int64_t)b * p.H + h) * p.nq + r] = acc;
+}
+
+// One fp32 per lane: rows [r0, r0 + 64) of a per-row vector into LDS.
+__device__ __forceinline__ void load_row_stats(char* lds, const float* base, int r0, int nrows,
+                                               int lane) {
+    const int row = min(r0 + lane, nrows - 1);
+    __builtin_amdgcn_global_load_lds(base + row, (FA_LDS void*)lds, 4, 0, 0);
+}
+
+// ---------------------------------------------------------------------------
+// 2. dK, dV (key-tile outer)
+template <int D, bool CAUSAL, bool VARLEN>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void fa_bwd_dkdv_kernel(AttnParams p) {
+    using C = BwdKVCfg<D>;
+    __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int h2 = lane >> 5;
+    const int col = lane & 31;
+    const int sl = lane & 15;
+    const int g = (lane >> 4) & 1;
+
+    const int L = xcd_logical_index(blockIdx.x, gridDim.x);
+    const int tile = L % p.n_tiles;        // low key tiles see the most query rows: first
+    const int bh = L / p.n_tiles;
+    const int h = bh % p.H;
+    const int b = bh / p.H;
+    int qs, nq, ks, nk;
+    seq_range<VARLEN>(p, b, qs, nq, ks, nk);
+    const int kv_start = tile * C::BN;
+    if (kv_start >= nk) return;
+    const int64_t tok = (int64_t)p.H * D;
+    const int kw0 = kv_start + wave * 32;   // this wave's first key
+    const int key = kw0 + col;              // this lane's key (accumulator column)
+
+    bf16x8 kf[C::KSTEPS], vf[C::KSTEPS];
+    {
+        const int64_t off = (int64_t)(ks + min(key, nk - 1)) * tok + h * D + 8 * h2;
+#pragma unroll
+        for (int s = 0; s < C::KSTEPS; ++s) {
+            kf[s] = load16(p.k + off + 16 * s);
+            vf[s] = load16(p.v + off + 16 * s);
+        }
+    }
+    f32x16 dka[C::DBLK], dva[C::DBLK];
+#pragma unroll
+    for (int cb = 0; cb < C::DBLK; ++cb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            dka[cb][r] = 0.f;
+            dva[cb][r] = 0.f;
+        }
+
+    const float c = p.scale_log2;
+    const bf16* qbase = p.q + (int64_t)qs * tok + h * D;
+    const bf16* gbase = p.dout + (int64_t)qs * tok + h * D;
+    const float* lbase = p.lse_in + ((int64_t)b * p.H + h) * p.nq;
+    const float* dbase = p.dvec + ((int64_t)b * p.H + h) * p.nq;
+    const int q_first = CAUSAL ? (kv_start / C::BMQ) * C::BMQ : 0;
+    const int n_q = nq > q_first ? (nq - q_first + C::BMQ - 1) / C::BMQ : 0;
+
+    auto issue = [&](int it) {
+        char* st = smem + (it & 1) * C::STAGE_BYTES;
+        const int q0 = q_first + it * C::BMQ;
+        load_tile_lds<D, C::BMQ, C::NW>(st, qbase, tok, q0, nq, wave, lane);
+        load_tile_lds<D, C::BMQ, C::NW>(st + C::TILE_BYTES, gbase, tok, q0, nq, wave, lane);
+        if (wave == 0) load_row_stats(st + 2 * C::TILE_BYTES, lbase, q0, nq, lane);
+        if (wave == 1) load_row_stats(st + 2 * C::TILE_BYTES + C::BMQ * 4, dbase, q0, nq, lane);
+    };
+
+    if (n_q > 0) issue(0);
+    for (int it = 0; it < n_q; ++it) {
+        char* st = smem + (it & 1) * C::STAGE_BYTES;
+        const char* qt = st;
+        const char* gt = st + C::TILE_BYTES;
+        const float* lse_t = reinterpret_cast<const float*>(st + 2 * C::TILE_BYTES);
+        const float* d_t = lse_t + C::BMQ;
+        wait_vmem();
+        __syncthreads();
+        if (it + 1 < n_q) issue(it + 1);
+        const int q0 = q_first + it * C::BMQ;
+
+#pragma unroll
+        for (int qb = 0; qb < C::BMQ / 32; ++qb) {
+            const int qb0 = q0 + qb * 32;
+            if (CAUSAL && qb0 + 31 < kw0) continue;   // every query here precedes every key
+
+            // S = Q K^T and dP = dO V^T: rows are queries, columns this wave's keys
+            f32x16 s, dp;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                s[r] = 0.f;
+                dp[r] = 0.f;
+            }
+            const int row = qb * 32 + col;
+#pragma unroll
+            for (int k2 = 0; k2 < C::KSTEPS; ++k2) {
+                const int off = tile_off<D>(row, 2 * k2 + h2);
+                s = mfma_32x32x16(lds_read16((const FA_LDS char*)(qt + off)), kf[k2], s);
+                dp = mfma_32x32x16(lds_read16((const FA_LDS char*)(gt + off)), vf[k2], dp);
+            }
+
+            // P = exp(scale*S - LSE), dS = P * (dP - D); this lane's rows are
+            // queries qb0 + 8*(r/4) + 4*h2 + r%4.
+            const bool need_mask = (CAUSAL && qb0 < kw0 + 31) || (qb0 + 31 >= nq);
+#pragma unroll
+            for (int rg = 0; rg < 4; ++rg) {
+                const int lr = qb * 32 + 8 * rg + 4 * h2;
+                const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse_t + lr);
+                const f32x4 d4 = *reinterpret_cast<const f32x4*>(d_t + lr);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 4 * rg + e;
+                    float pr = fast_exp2(__builtin_fmaf(s[r], c, -l4[e] * kLog2e));
+                    if (need_mask) {
+                        const int qrow = qb0 + 8 * rg + 4 * h2 + e;
+                        if ((CAUSAL && key > qrow) || qrow >= nq) pr = 0.f;
+                    }
+                    s[r] = pr;
+                    dp[r] = pr * (dp[r] - d4[e]);
+                }
+            }
+            bf16x8 pb[2], db[2];
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                float tp[8], td[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    tp[e] = s[8 * kk + e];
+                    td[e] = dp[8 * kk + e];
+                }
+                pb[kk] = pack8(tp);
+                db[kk] = pack8(td);
+            }
+
+            // dV^T[dim][key] += dO^T P,  dK^T[dim][key] += Q^T dS
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                const int r1 = qb * 32 + 16 * kk + 4 * h2;
+#pragma unroll
+                for (int cb = 0; cb < C::DBLK; ++cb) {
+                    const int c0 = cb * 32 + 16 * g;
+                    const int o1 = tr_off<D>(r1, c0, sl);
+                    const int o2 = tr_off<D>(r1 + 8, c0, sl);
+                    const bf16x8 ag = join(lds_read_tr((const FA_LDS char*)(gt + o1)),
+                                           lds_read_tr((const FA_LDS char*)(gt + o2)));
+                    dva[cb] = mfma_32x32x16(ag, pb[kk], dva[cb]);
+                    const bf16x8 aq = join(lds_read_tr((const FA_LDS char*)(qt + o1)),
+                                           lds_read_tr((const FA_LDS char*)(qt + o2)));
+                    dka[cb] = mfma_32x32x16(aq, db[kk], dka[cb]);
+                }
+            }
+        }
+    }
+
+    if (key < nk) {
+        const int64_t off = (int64_t)(ks + key) * tok + h * D;
+        const float sc = p.scale;
+#pragma unroll
+        for (int cb = 0; cb < C::DBLK; ++cb)
+#pragma unroll
+            for (int rg = 0; rg < 4; ++rg) {
+                const int d0 = cb * 32 + 8 * rg + 4 * h2;
+                store8(p.dk + off + d0, dka[cb][4 * rg] * sc, dka[cb][4 * rg + 1] * sc,
+                       dka[cb][4 * rg + 2] * sc, dka[cb][4 * rg + 3] * sc);
+                store8(p.dv + off + d0, dva[cb][4 * rg], dva[cb][4 * rg + 1], dva[cb][4 * rg + 2],
+                       dva[cb][4 * rg + 3]);
+            }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// 3. dQ (query-tile outer)
+template <int D, bool CAUSAL, bool VARLEN>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void fa_bwd_dq_kernel(AttnParams p) {
+    using C = BwdQCfg<D>;
+    __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int h2 = lane >> 5;
+    const int col = lane & 31;
+    const int sl = lane & 15;
+    const int g = (lane >> 4) & 1;
+
+    const int L = xcd_logical_index(blockIdx.x, gridDim.x);
+    const int tile = p.n_tiles - 1 - (L % p.n_tiles);
+    const int bh = L / p.n_tiles;
+    const int h = bh % p.H;
+    const int b = bh / p.H;
+    int qs, nq, ks, nk;
+    seq_range<VARLEN>(p, b, qs, nq, ks, nk);
+    const int q_start = tile * C::BM;
+    if (q_start >= nq) return;
+    const int kv_end = CAUSAL ? min(nk, q_start + C::BM) : nk;
+    const int n_kv = (kv_end + C::BN - 1) / C::BN;
+    const int64_t tok = (int64_t)p.H * D;
+    const bf16* kbase = p.k + (int64_t)ks * tok + h * D;
+    const bf16* vbase = p.v + (int64_t)ks * tok + h * D;
+
+    const int qw0 = q_start + wave * 32;
+    const int qi = qw0 + col;
+    const int qrow = min(qi, nq - 1);
+    bf16x8 qf[C::KSTEPS], gf[C::KSTEPS];
+    {
+        const int64_t off = (int64_t)(qs + qrow) * tok + h * D + 8 * h2;
+#pragma unroll
+        for (int s = 0; s < C::KSTEPS; ++s) {
+            qf[s] = load16(p.q + off + 16 * s);
+            gf[s] = load16(p.dout + off + 16 * s);
+        }
+    }
+    const int64_t srow = ((int64_t)b * p.H + h) * p.nq + qrow;
+    const float lse2 = p.lse_in[srow] * kLog2e;
+    const float dd = p.dvec[srow];
+    const float c = p.scale_log2;
+
+    f32x16 acc[C::DBLK];
+#pragma unroll
+    for (int cb = 0; cb < C::DBLK; ++cb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[cb][r] = 0.f;
+
+    if (n_kv > 0) {
+        load_tile_lds<D, C::BN, C::NW>(smem, kbase, tok, 0, nk, wave, lane);
+        load_tile_lds<D, C::BN, C::NW>(smem + C::TILE_BYTES, vbase, tok, 0, nk, wave, lane);
+    }
+    for (int t = 0; t < n_kv; ++t) {
+        char* kt = smem + (t & 1) * 2 * C::TILE_BYTES;
+        char* vt = kt + C::TILE_BYTES;
+        wait_vmem();
+        __syncthreads();
+        if (t + 1 < n_kv) {
+            char* kn = smem + ((t + 1) & 1) * 2 * C::TILE_BYTES;
+            load_tile_lds<D, C::BN, C::NW>(kn, kbase, tok, (t + 1) * C::BN, nk, wave, lane);
+            load_tile_lds<D, C::BN, C::NW>(kn + C::TILE_BYTES, vbase, tok, (t + 1) * C::BN, nk, wave,
+                                           lane);
+        }
+        const int kv0 = t * C::BN;
+        if (CAUSAL && kv0 > qw0 + 31) continue;
+
+        // S^T = K Q^T, dP^T = V dO^T: rows keys, columns this wave's queries
+        f32x16 sT[C::KB], dpT[C::KB];
+#pragma unroll
+        for (int kb = 0; kb < C::KB; ++kb) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                sT[kb][r] = 0.f;
+                dpT[kb][r] = 0.f;
+            }
+            const int row = kb * 32 + col;
+#pragma unroll
+            for (int k2 = 0; k2 < C::KSTEPS; ++k2) {
+                const int off = tile_off<D>(row, 2 * k2 + h2);
+                sT[kb] = mfma_32x32x16(lds_read16((const FA_LDS char*)(kt + off)), qf[k2], sT[kb]);
+                dpT[kb] = mfma_32x32x16(lds_read16((const FA_LDS char*)(vt + off)), gf[k2], dpT[kb]);
+            }
+        }
+        const bool need_mask = (CAUSAL && kv0 + C::BN - 1 > qw0) || (kv0 + C::BN > nk);
+#pragma unroll
+        for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                float pr = fast_exp2(__builtin_fmaf(sT[kb][r], c, -lse2));
+                if (need_mask) {
+                    const int kj = kv0 + kb * 32 + 8 * (r >> 2) + 4 * h2 + (r & 3);
+                    if ((CAUSAL && kj > qi) || kj >= nk) pr = 0.f;
+                }
+                sT[kb][r] = pr * (dpT[kb][r] - dd);   // dS^T
+            }
+        bf16x8 dsk[C::BN / 16];
+#pragma unroll
+        for (int k2 = 0; k2 < C::BN / 16; ++k2) {
+            float tmp[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) tmp[e] = sT[k2 >> 1][8 * (k2 & 1) + e];
+            dsk[k2] = pack8(tmp);
+        }
+        // dQ^T[dim][query] += K^T dS^T, K^T via transposed LDS reads
+#pragma unroll
+        for (int k2 = 0; k2 < C::BN / 16; ++k2) {
+            const int r1 = 16 * k2 + 4 * h2;
+#pragma unroll
+            for (int cb = 0; cb < C::DBLK; ++cb) {
+                const int c0 = cb * 32 + 16 * g;
+                const bf16x8 a = join(lds_read_tr((const FA_LDS char*)(kt + tr_off<D>(r1, c0, sl))),
+                                      lds_read_tr((const FA_LDS char*)(kt + tr_off<D>(r1 + 8, c0, sl))));
+                acc[cb] = mfma_32x32x16(a, dsk[k2], acc[cb]);
+            }
+        }
+    }
+
+    if (qi < nq) {
+        bf16* optr = p.dq + (int64_t)(qs + qi) * tok + h * D;
+        const float sc = p.scale;
+#pragma unroll
+        for (int cb = 0; cb < C::DBLK; ++cb)
+#pragma unroll
+            for (int rg = 0; rg < 4; ++rg) {
+                const int d0 = cb * 32 + 8 * rg + 4 * h2;
+                store8(optr + d0, acc[cb][4 * rg] * sc, acc[cb][4 * rg + 1] * sc,
+                       acc[cb][4 * rg + 2] * sc, acc[cb][4 * rg + 3] * sc);
+            }
+    }
+}
+
+}  // namespace fa355

@@ -1,0 +1,113 @@
+// Device primitives for gfx950 (CDNA4): MFMA tiles, wave64 cross-half exchange,
+// direct global->LDS loads, transposed LDS reads and bf16 packing.
+//
+// Operand layouts of v_mfma_f32_32x32x16_bf16 (C[32x32] += A[32x16] * B[16x32]),
+// for lane l of a 64-wide wave, half h = l / 32:
+//   A: lane l holds A[l % 32][8h .. 8h+7]
+//   B: lane l holds B[8h .. 8h+7][l % 32]
+//   C: lane l, register r holds C[8*(r/4) + 4h + (r%4)][l % 32]
+// The sum index k may be permuted freely as long as A and B agree on it; the
+// kernels use that to feed an accumulator tile straight back in as an operand.
+//
+// ds_read_b64_tr_b16: within each group of 16 lanes, lane s names 8 bytes (4 bf16)
+// of a 4 x 16 block (row s/4, columns 4*(s%4)..+3); lane i receives column i of
+// that block (its 4 rows).  Reading a row-major [key][dim] tile this way yields
+// four consecutive keys of one dimension per lane, i.e. the operand a product over
+// keys needs.
+//
+// global_load_lds_dwordx4: each lane fetches 16 bytes from its own global
+// address; lane l's bytes land at (LDS base + 16*l), base uniform over the wave.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa355 {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+#define FA_LDS __attribute__((address_space(3)))
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_huge_valf();
+
+__device__ __forceinline__ f32x16 mfma_32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Value held by lane (l ^ 32) of the same register, via v_permlane32_swap.
+// Only the lane-dependent select of one result is used: combining both results
+// of the swap directly in one arithmetic operation (max(r0, r1), r0 + r1) is
+// miscompiled by the ROCm 7.2 compiler for gfx950 (it reuses r0 for r1).
+__device__ __forceinline__ float other_half(float x) {
+    const uint32_t u = __builtin_bit_cast(uint32_t, x);
+    auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    // lanes 0-31 receive the upper half in r[1]; lanes 32-63 the lower half in r[0]
+    return __builtin_bit_cast(float, (__lane_id() < 32) ? r[1] : r[0]);
+}
+
+__device__ __forceinline__ float max_halves(float x) { return fmaxf(x, other_half(x)); }
+
+__device__ __forceinline__ float sum_halves(float x) { return x + other_half(x); }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Round-to-nearest-even pack of two floats (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    bf16x2 p = (bf16x2){(bf16)a, (bf16)b};
+    return __builtin_bit_cast(uint32_t, p);
+}
+
+// 8 consecutive accumulator floats -> one bf16x8 operand.
+__device__ __forceinline__ bf16x8 pack8(const float* f) {
+    u32x4 u = (u32x4){pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]),
+                      pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7])};
+    return __builtin_bit_cast(bf16x8, u);
+}
+
+__device__ __forceinline__ bf16x8 load16(const bf16* p) {
+    return *reinterpret_cast<const bf16x8*>(p);
+}
+
+__device__ __forceinline__ void store8(bf16* p, float a, float b, float c, float d) {
+    u32x2 u = (u32x2){pack_bf16x2(a, b), pack_bf16x2(c, d)};
+    *reinterpret_cast<u32x2*>(p) = u;
+}
+
+__device__ __forceinline__ void global_to_lds16(const void* g, FA_LDS void* lds_wave_base) {
+    __builtin_amdgcn_global_load_lds(g, lds_wave_base, 16, 0, 0);
+}
+
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+__device__ __forceinline__ bf16x8 lds_read16(const FA_LDS char* p) {
+    return *reinterpret_cast<const FA_LDS bf16x8*>(p);
+}
+
+__device__ __forceinline__ bf16x4 lds_read_tr(const FA_LDS char* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+        reinterpret_cast<FA_LDS bf16x4*>(const_cast<FA_LDS char*>(p)));
+}
+
+__device__ __forceinline__ bf16x8 join(bf16x4 lo, bf16x4 hi) {
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Work-item order over a 1-D grid of `total` work-groups.  Consecutive
+// work-group ids are spread round-robin over the 8 XCDs (each with its own L2);
+// this maps XCD x to the contiguous logical range [x*total/8, (x+1)*total/8), so
+// the work-groups resident on one XCD share the same few heads' K/V in L2.
+__device__ __forceinline__ int xcd_logical_index(int id, int total) {
+    if ((total & 7) != 0) return id;
+    return (id & 7) * (total >> 3) + (id >> 3);
+}
+
+}  // namespace fa355

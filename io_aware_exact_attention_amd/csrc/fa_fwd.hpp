@@ -1,0 +1,209 @@
+// Forward kernel: O = softmax(scale * Q K^T) V and LSE, without writing S or P.
+//
+// Method ("08 · FlashAttention", §二; "LLM Systems 22: Flash Attention", §3.1):
+// each work-group owns a tile of BM query rows and streams the key/value rows in
+// tiles of BN.  Per query row it keeps a running maximum m, a running sum l and an
+// unnormalised accumulator O; a new tile with scores S' updates them as
+//     m_new = max(m, rowmax S'),  P~ = exp(S' - m_new),
+//     l <- e^(m - m_new) l + rowsum P~,   O <- e^(m - m_new) O + P~ V',
+// and O / l is written once at the end with LSE = m + ln l.  Work is done in the
+// base-2 domain: exp(x*scale) = exp2(x * scale*log2 e), the scale folded into
+// one FMA per score.  With the causal mask only key tiles at or below the
+// diagonal are visited, and only tiles that straddle it are masked.
+//
+// gfx950 mapping (one work-group = 4 waves = BM 128 query rows, 32 per wave):
+//   * Q rows stay in registers for the whole kernel as the B operand of
+//     S^T = K Q^T (v_mfma_f32_32x32x16_bf16, fp32 accumulation).
+//   * K and V tiles (BN = 64 rows) stream from HBM into LDS with direct
+//     global->LDS 16-byte loads, double-buffered so the next tile's load
+//     overlaps this tile's math; one barrier per tile.
+//   * Because S^T's accumulator gives each lane one query and 16 keys per
+//     32-key block, the row max/sum are in-lane reductions plus one
+//     permlane32 swap, the rescale factor is lane-local, and the probabilities
+//     feed the P V product (computed as O^T = V^T P^T) directly as the B
+//     operand, with no LDS round trip.  V^T's operand comes from LDS through
+//     the transposing ds_read_b64_tr_b16.
+//   * LDS tiles are XOR-swizzled at 16-byte granularity so that both the
+//     row-wise K reads and the transposed V reads are free of bank conflicts.
+#pragma once
+
+#include "fa_tiles.hpp"
+
+namespace fa355 {
+
+template <int D>
+struct FwdCfg {
+    static constexpr int NW = 4;                 // waves per work-group
+    static constexpr int BM = 32 * NW;           // query rows per work-group
+    static constexpr int BN = 64;                // key rows per tile
+    static constexpr int ROW_BYTES = D * 2;
+    static constexpr int CPR = D / 8;            // 16-byte chunks per row
+    static constexpr int TILE_BYTES = BN * ROW_BYTES;
+    static constexpr int KSTEPS = D / 16;        // MFMA k-steps over the head dim
+    static constexpr int DBLK = D / 32;          // 32-wide blocks of the head dim
+    static constexpr int KB = BN / 32;           // 32-key blocks per tile
+    static constexpr int LDS_BYTES = 2 * 2 * TILE_BYTES;   // [buffer][K | V]
+};
+
+template <int D, bool CAUSAL, bool VARLEN>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void fa_fwd_kernel(AttnParams p) {
+    using C = FwdCfg<D>;
+    __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int h2 = lane >> 5;
+    const int col = lane & 31;
+
+    const int L = xcd_logical_index(blockIdx.x, gridDim.x);
+    const int tile = p.n_tiles - 1 - (L % p.n_tiles);   // longest causal rows first
+    const int bh = L / p.n_tiles;
+    const int h = bh % p.H;
+    const int b = bh / p.H;
+    int qs, nq, ks, nk;
+    seq_range<VARLEN>(p, b, qs, nq, ks, nk);
+    const int q_start = tile * C::BM;
+    if (q_start >= nq) return;
+    const int kv_end = CAUSAL ? min(nk, q_start + C::BM) : nk;
+    const int n_kv = (kv_end + C::BN - 1) / C::BN;
+    const int64_t tok = (int64_t)p.H * D;
+    const bf16* kbase = p.k + (int64_t)ks * tok + h * D;
+    const bf16* vbase = p.v + (int64_t)ks * tok + h * D;
+
+    const int qw0 = q_start + wave * 32;   // first query row of this wave
+    const int qi = qw0 + col;              // this lane's query row
+    const bf16* qptr = p.q + (int64_t)(qs + min(qi, nq - 1)) * tok + h * D + 8 * h2;
+    bf16x8 qf[C::KSTEPS];
+#pragma unroll
+    for (int s = 0; s < C::KSTEPS; ++s) qf[s] = load16(qptr + 16 * s);
+
+    f32x16 acc[C::DBLK];
+#pragma unroll
+    for (int cb = 0; cb < C::DBLK; ++cb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[cb][r] = 0.f;
+    float m = kNegInf;   // running max of raw scores q.k (this row)
+    float l = 0.f;       // running sum, over the keys this lane holds
+    const float c = p.scale_log2;
+
+    if (n_kv > 0) {
+        load_tile_lds<D, C::BN, C::NW>(smem, kbase, tok, 0, nk, wave, lane);
+        load_tile_lds<D, C::BN, C::NW>(smem + C::TILE_BYTES, vbase, tok, 0, nk, wave, lane);
+    }
+    for (int t = 0; t < n_kv; ++t) {
+        char* kt = smem + (t & 1) * 2 * C::TILE_BYTES;
+        char* vt = kt + C::TILE_BYTES;
+        wait_vmem();
+        __syncthreads();
+        if (t + 1 < n_kv) {
+            char* kn = smem + ((t + 1) & 1) * 2 * C::TILE_BYTES;
+            load_tile_lds<D, C::BN, C::NW>(kn, kbase, tok, (t + 1) * C::BN, nk, wave, lane);
+            load_tile_lds<D, C::BN, C::NW>(kn + C::TILE_BYTES, vbase, tok, (t + 1) * C::BN, nk,
+                                                 wave, lane);
+        }
+        const int kv0 = t * C::BN;
+        if (CAUSAL && kv0 > qw0 + 31) continue;   // every key here is above this wave's rows
+
+        // S^T[key][query] = K Q^T for the tile's 64 keys
+        f32x16 s[C::KB];
+#pragma unroll
+        for (int kb = 0; kb < C::KB; ++kb) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+            const int row = kb * 32 + col;
+#pragma unroll
+            for (int st = 0; st < C::KSTEPS; ++st) {
+                bf16x8 a = lds_read16((const FA_LDS char*)(kt + tile_off<D>(row, 2 * st + h2)));
+                s[kb] = mfma_32x32x16(a, qf[st], s[kb]);
+            }
+        }
+
+        // causal diagonal / ragged tail
+        const bool need_mask = (CAUSAL && kv0 + C::BN - 1 > qw0) || (kv0 + C::BN > nk);
+        if (need_mask) {
+#pragma unroll
+            for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int key = kv0 + kb * 32 + 8 * (r >> 2) + 4 * h2 + (r & 3);
+                    if ((CAUSAL && key > qi) || key >= nk) s[kb][r] = kNegInf;
+                }
+        }
+
+        float mx = kNegInf;
+#pragma unroll
+        for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+        mx = max_halves(mx);
+        const float m_new = fmaxf(m, mx);
+        const float m_ref = (m_new == kNegInf) ? 0.f : m_new;
+        const float alpha = fast_exp2((m - m_ref) * c);
+        const float mc = m_ref * c;
+        float rs = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float pr = fast_exp2(__builtin_fmaf(s[kb][r], c, -mc));
+                s[kb][r] = pr;
+                rs += pr;
+            }
+        l = l * alpha + rs;
+        m = m_new;
+        if (wave_any(alpha != 1.f)) {
+#pragma unroll
+            for (int cb = 0; cb < C::DBLK; ++cb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[cb][r] *= alpha;
+        }
+
+        // P^T operand: registers 8*(ks&1)..+7 of key block ks/2 hold keys
+        // 16*ks + {4*h2 + 0..3, 8 + 4*h2 + 0..3} for this lane's query.
+        bf16x8 pk[C::BN / 16];
+#pragma unroll
+        for (int ks2 = 0; ks2 < C::BN / 16; ++ks2) {
+            float tmp[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) tmp[e] = s[ks2 >> 1][8 * (ks2 & 1) + e];
+            pk[ks2] = pack8(tmp);
+        }
+
+        // O^T[dim][query] += V^T P^T; V^T operand via transposed LDS reads of the
+        // same key order: rows 16*ks + 4*h2 + 0..3 and +8.
+        const int sl = lane & 15;
+        const int g = (lane >> 4) & 1;
+#pragma unroll
+        for (int ks2 = 0; ks2 < C::BN / 16; ++ks2) {
+            const int r1 = 16 * ks2 + 4 * h2;
+#pragma unroll
+            for (int cb = 0; cb < C::DBLK; ++cb) {
+                const int c0 = cb * 32 + 16 * g;
+                bf16x8 a = join(lds_read_tr((const FA_LDS char*)(vt + tr_off<D>(r1, c0, sl))),
+                                lds_read_tr((const FA_LDS char*)(vt + tr_off<D>(r1 + 8, c0, sl))));
+                acc[cb] = mfma_32x32x16(a, pk[ks2], acc[cb]);
+            }
+        }
+    }
+
+    const float lt = sum_halves(l);
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    if (qi < nq) {
+        bf16* optr = p.o + (int64_t)(qs + qi) * tok + h * D;
+#pragma unroll
+        for (int cb = 0; cb < C::DBLK; ++cb)
+#pragma unroll
+            for (int rg = 0; rg < 4; ++rg) {
+                const int d0 = cb * 32 + 8 * rg + 4 * h2;
+                store8(optr + d0, acc[cb][4 * rg] * inv, acc[cb][4 * rg + 1] * inv,
+                       acc[cb][4 * rg + 2] * inv, acc[cb][4 * rg + 3] * inv);
+            }
+        if (h2 == 0) {
+            p.lse[((int64_t)b * p.H + h) * p.nq + qi] =
+                lt > 0.f ? (m * c + __builtin_amdgcn_logf(lt)) * kLn2 : kNegInf;
+        }
+    }
+}
+
+}  // namespace fa355

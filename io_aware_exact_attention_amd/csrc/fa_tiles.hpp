@@ -1,0 +1,61 @@
+// LDS tile layout and streaming shared by the forward and backward kernels.
+#pragma once
+
+#include "fa_params.hpp"
+
+namespace fa355 {
+
+// LDS tiles are row-major [row][D] bf16 with the 16-byte chunks of each row
+// permuted: logical chunk c of row r sits at physical chunk c ^ tile_swz(r).  The
+// XOR keeps 32-byte segments' halves adjacent except on odd XOR values, and is
+// chosen so that (a) 16 consecutive rows read at one logical chunk (row-wise
+// operand reads, ds_read_b128) and (b) 8 consecutive rows read at two adjacent
+// chunks (transposed operand reads, ds_read_b64_tr_b16) all hit distinct banks.
+template <int D>
+__device__ __forceinline__ int tile_swz(int row) {
+    if constexpr (D == 128) return 2 * (row & 7) + ((row >> 3) & 1);
+    else return 2 * ((row >> 1) & 3) + ((row >> 3) & 1);
+}
+
+// Byte offset of the 16-byte chunk holding logical chunk `chunk` of `row`.
+template <int D>
+__device__ __forceinline__ int tile_off(int row, int chunk) {
+    return row * D * 2 + 16 * (chunk ^ tile_swz<D>(row));
+}
+
+// Byte offset a lane passes to ds_read_b64_tr_b16 for a 4 x 16 block whose rows
+// start at `row0` (multiple of 4) and whose columns start at `col0` (multiple of
+// 16): lane s of the 16-lane group names row row0 + s/4, columns col0 + 4*(s%4).
+template <int D>
+__device__ __forceinline__ int tr_off(int row0, int col0, int sl) {
+    const int row = row0 + (sl >> 2);
+    const int col = col0 + 4 * (sl & 3);
+    return tile_off<D>(row, col >> 3) + 2 * (col & 7);
+}
+
+// Stream rows [r0, r0 + ROWS) of a [rows x D] bf16 tile into LDS (wave-cooperative:
+// every wave covers a disjoint 1 KB slice per instruction).  Rows past `nrows`
+// are clamped to the last valid row (finite data; the consumer masks them).
+template <int D, int ROWS, int NW>
+__device__ __forceinline__ void load_tile_lds(char* lds_tile, const bf16* base, int64_t row_stride,
+                                              int r0, int nrows, int wave, int lane) {
+    constexpr int CPR = D / 8;
+    constexpr int ROWS_PER_INST = 1024 / (D * 2);
+    constexpr int INSTS = ROWS * D * 2 / 1024 / NW;
+    static_assert(ROWS * D * 2 % (1024 * NW) == 0, "tile must split evenly over waves");
+#pragma unroll
+    for (int i = 0; i < INSTS; ++i) {
+        const int inst = wave * INSTS + i;
+        const int r = inst * ROWS_PER_INST + lane / CPR;
+        const int lc = (lane % CPR) ^ tile_swz<D>(r);   // logical chunk stored in this slot
+        const int row = min(r0 + r, nrows - 1);
+        global_to_lds16(base + (int64_t)row * row_stride + lc * 8,
+                        (FA_LDS void*)(lds_tile + inst * 1024));
+    }
+}
+
+__device__ __forceinline__ bool wave_any(bool pred) {
+    return __builtin_amdgcn_ballot_w64(pred) != 0;
+}
+
+}  // namespace fa355

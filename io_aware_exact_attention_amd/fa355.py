@@ -1,0 +1,176 @@
+"""Python binding of libfa355 (ctypes).  Argument marshalling only.
+
+The functions named like the C entry points (``fa_fwd``, ``fa_bwd``,
+``fa_fwd_varlen``, ``fa_bwd_varlen``, ``fa_bwd_workspace_bytes``,
+``fa_status_string``) take torch tensors that already live on the GPU, pass
+their device pointers and sizes to the library on the current torch stream,
+and raise ``FaError`` on a non-zero status.  Every computation happens in the
+library's HIP kernels; there is no other code path, and a missing or
+unloadable library raises immediately.
+
+``attention_forward`` / ``attention_backward`` (and the varlen variants) are
+conveniences that allocate the outputs with torch and call the entry points.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa355.so")
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "fa355.h")
+
+_c_int, _c_float, _vp, _sz = ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
+
+_SIGNATURES = {
+    "fa_status_string": (ctypes.c_char_p, [_c_int]),
+    "fa_version": (_c_int, []),
+    "fa_fwd": (_c_int, [_vp] * 5 + [_c_int] * 5 + [_c_float, _c_int, _vp]),
+    "fa_fwd_varlen": (_c_int, [_vp] * 7 + [_c_int] * 5 + [_c_float, _c_int, _vp]),
+    "fa_bwd_workspace_bytes": (_sz, [_c_int] * 4),
+    "fa_bwd": (_c_int, [_vp] * 10 + [_sz] + [_c_int] * 5 + [_c_float, _c_int, _vp]),
+    "fa_bwd_varlen": (_c_int, [_vp] * 10 + [_sz] + [_vp] * 2 + [_c_int] * 5 + [_c_float, _c_int, _vp]),
+}
+
+STATUS = {0: "FA_OK", -1: "FA_ERR_NULL", -2: "FA_ERR_SHAPE", -3: "FA_ERR_UNSUPPORTED",
+          -4: "FA_ERR_ALIGN", -5: "FA_ERR_LAUNCH", -6: "FA_ERR_WORKSPACE"}
+
+_lib = None
+
+
+class FaError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"libfa355 error {status}: {msg}")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (raises if it is not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m io_aware_exact_attention_amd.build`")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def header_functions() -> list[str]:
+    """Names of the functions include/fa355.h declares."""
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_]+\s*\*?\s*(fa_[a-z0-9_]+)\s*\(", text, re.M)))
+
+
+def fa_status_string(status: int) -> str:
+    return lib().fa_status_string(int(status)).decode()
+
+
+def _check(status: int):
+    if status != 0:
+        raise FaError(status, fa_status_string(status))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dense_dims(q, k):
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("dense tensors are [B, N, H, d]")
+    B, Nq, H, d = q.shape
+    return B, H, Nq, k.shape[1], d
+
+
+def fa_fwd(q, k, v, o, lse, scale: float, causal: bool, stream=None):
+    B, H, Nq, Nk, d = _dense_dims(q, k)
+    _check(lib().fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Nq, Nk, d,
+                        float(scale), int(bool(causal)), _stream(stream)))
+
+
+def fa_bwd_workspace_bytes(batch_or_nseq: int, H: int, nq: int, d: int) -> int:
+    return int(lib().fa_bwd_workspace_bytes(int(batch_or_nseq), int(H), int(nq), int(d)))
+
+
+def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, scale: float, causal: bool, stream=None):
+    B, H, Nq, Nk, d = _dense_dims(q, k)
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(lib().fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq),
+                        _ptr(dk), _ptr(dv), _ptr(workspace), nbytes, B, H, Nq, Nk, d,
+                        float(scale), int(bool(causal)), _stream(stream)))
+
+
+def fa_fwd_varlen(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int,
+                  max_seqlen_k: int, scale: float, causal: bool, stream=None):
+    nseq = cu_seqlens_q.numel() - 1
+    _check(lib().fa_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(cu_seqlens_q),
+                               _ptr(cu_seqlens_k), nseq, int(max_seqlen_q), int(max_seqlen_k),
+                               q.shape[1], q.shape[2], float(scale), int(bool(causal)),
+                               _stream(stream)))
+
+
+def fa_bwd_varlen(q, k, v, o, dout, lse, dq, dk, dv, workspace, cu_seqlens_q, cu_seqlens_k,
+                  max_seqlen_q: int, max_seqlen_k: int, scale: float, causal: bool, stream=None):
+    nseq = cu_seqlens_q.numel() - 1
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(lib().fa_bwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse),
+                               _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), nbytes,
+                               _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), nseq, int(max_seqlen_q),
+                               int(max_seqlen_k), q.shape[1], q.shape[2], float(scale),
+                               int(bool(causal)), _stream(stream)))
+
+
+# ---------------------------------------------------------------------------
+# conveniences: allocate outputs (device memory via torch), then call the ABI
+
+def attention_forward(q, k, v, scale: float, causal: bool):
+    B, H, Nq, Nk, d = _dense_dims(q, k)
+    o = torch.empty_like(q)
+    lse = torch.empty(B, H, Nq, dtype=torch.float32, device=q.device)
+    fa_fwd(q, k, v, o, lse, scale, causal)
+    return o, lse
+
+
+def attention_backward(q, k, v, o, dout, lse, scale: float, causal: bool, workspace=None):
+    B, H, Nq, Nk, d = _dense_dims(q, k)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    if workspace is None:
+        nbytes = fa_bwd_workspace_bytes(B, H, Nq, d)
+        workspace = torch.empty(nbytes // 4, dtype=torch.float32, device=q.device)
+    fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, scale, causal)
+    return dq, dk, dv
+
+
+def attention_forward_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
+                             scale: float, causal: bool):
+    nseq = cu_seqlens_q.numel() - 1
+    o = torch.empty_like(q)
+    lse = torch.empty(nseq, q.shape[1], max_seqlen_q, dtype=torch.float32, device=q.device)
+    fa_fwd_varlen(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
+                  scale, causal)
+    return o, lse
+
+
+def attention_backward_varlen(q, k, v, o, dout, lse, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
+                              max_seqlen_k, scale: float, causal: bool, workspace=None):
+    nseq = cu_seqlens_q.numel() - 1
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    if workspace is None:
+        nbytes = fa_bwd_workspace_bytes(nseq, q.shape[1], max_seqlen_q, q.shape[2])
+        workspace = torch.empty(nbytes // 4, dtype=torch.float32, device=q.device)
+    fa_bwd_varlen(q, k, v, o, dout, lse, dq, dk, dv, workspace, cu_seqlens_q, cu_seqlens_k,
+                  max_seqlen_q, max_seqlen_k, scale, causal)
+    return dq, dk, dv

@@ -1,0 +1,97 @@
+"""The C-ABI library: it loads, exports every declared entry point, and rejects
+bad arguments on the host before any GPU work (CPU only: every call below fails
+validation, so nothing is launched)."""
+
+import ctypes
+import subprocess
+
+import pytest
+
+from io_aware_exact_attention_amd import fa355
+
+A = 0x10000        # a 16-byte-aligned fake device address (never dereferenced)
+MIS = 0x10008      # 8-byte aligned only
+
+
+def _fwd(q=A, k=A, v=A, o=A, lse=A, B=1, H=1, Nq=16, Nk=16, d=64, scale=0.125, causal=0):
+    return fa355.lib().fa_fwd(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, None)
+
+
+def _bwd(ptrs=None, ws=A, wsb=1 << 20, B=1, H=1, Nq=16, Nk=16, d=64, scale=0.125, causal=0):
+    p = ptrs or [A] * 9
+    return fa355.lib().fa_bwd(*p, ws, wsb, B, H, Nq, Nk, d, scale, causal, None)
+
+
+def _fwd_varlen(cu=A, nseq=2, mq=16, mk=16, H=1, d=64, scale=0.125, causal=0, o=A):
+    return fa355.lib().fa_fwd_varlen(A, A, A, o, A, cu, cu, nseq, mq, mk, H, d, scale, causal, None)
+
+
+def test_exports_every_declared_function():
+    names = fa355.header_functions()
+    assert set(names) >= {"fa_fwd", "fa_bwd", "fa_fwd_varlen", "fa_bwd_varlen",
+                          "fa_bwd_workspace_bytes", "fa_status_string", "fa_version"}
+    out = subprocess.run(["nm", "-D", "--defined-only", fa355.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    for n in names:
+        assert n in exported, f"{n} declared in fa355.h but not exported"
+        assert hasattr(fa355.lib(), n)
+
+
+def test_status_strings_and_version():
+    for code, name in fa355.STATUS.items():
+        assert fa355.fa_status_string(code).startswith(name)
+    assert fa355.fa_status_string(-99) == "FA_ERR_UNKNOWN"
+    assert fa355.lib().fa_version() >= 100
+
+
+def test_workspace_bytes():
+    assert fa355.fa_bwd_workspace_bytes(8, 16, 4096, 128) == 4 * 8 * 16 * 4096
+    assert fa355.fa_bwd_workspace_bytes(0, 16, 4096, 128) == 0
+    assert fa355.fa_bwd_workspace_bytes(2, -1, 4, 64) == 0
+
+
+@pytest.mark.parametrize("arg", ["q", "k", "v", "o", "lse"])
+def test_fwd_null(arg):
+    assert _fwd(**{arg: None}) == -1
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=0), -2), (dict(H=0), -2), (dict(Nq=0), -2), (dict(Nk=-3), -2),
+    (dict(d=96), -3), (dict(d=256), -3), (dict(d=32), -3),
+    (dict(causal=1, Nq=16, Nk=32), -3), (dict(causal=2), -3),
+    (dict(scale=0.0), -3), (dict(scale=float("nan")), -3), (dict(scale=float("inf")), -3),
+    (dict(q=MIS), -4), (dict(o=MIS), -4), (dict(lse=A + 2), -4),
+    (dict(B=1 << 20, Nq=1 << 20, Nk=1 << 20), -2),
+])
+def test_fwd_rejects(kw, code):
+    assert _fwd(**kw) == code
+
+
+def test_bwd_rejects():
+    assert _bwd(ptrs=[A] * 8 + [None]) == -1
+    assert _bwd(ws=None) == -6
+    assert _bwd(wsb=4 * 16 - 1) == -6
+    assert _bwd(d=80) == -3
+    assert _bwd(causal=1, Nk=8) == -3
+    assert _bwd(ptrs=[A] * 6 + [MIS] + [A] * 2) == -4
+    assert _bwd(ws=A + 2) == -4
+    assert _bwd(Nq=0) == -2
+
+
+def test_varlen_rejects():
+    assert _fwd_varlen(cu=None) == -1
+    assert _fwd_varlen(nseq=0) == -2
+    assert _fwd_varlen(mq=0) == -2
+    assert _fwd_varlen(d=48) == -3
+    assert _fwd_varlen(cu=A + 2) == -4
+    assert _fwd_varlen(o=MIS) == -4
+    lib = fa355.lib()
+    assert lib.fa_bwd_varlen(*[A] * 9, A, 4, A, A, 2, 16, 16, 1, 64, 0.1, 0, None) == -6
+    assert lib.fa_bwd_varlen(*[A] * 9, A, 1 << 20, None, A, 2, 16, 16, 1, 64, 0.1, 0, None) == -1
+
+
+def test_binding_raises_on_error():
+    with pytest.raises(fa355.FaError) as e:
+        fa355._check(-3)
+    assert e.value.status == -3

@@ -1,0 +1,143 @@
+"""HIP path vs CPU oracle, element by element, on seeded inputs (GPU).
+
+Small and ragged shapes are compared in full; the large workloads are run at
+full size in the same launch configuration the benchmark uses and compared on
+whole sampled (batch, head) slices, which the oracle computes exactly because
+heads are independent.
+"""
+
+import pytest
+import torch
+
+from io_aware_exact_attention_amd import fa355, workloads as wl
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+
+DENSE_CASES = [
+    # B, Nq, Nk, H, d, causal
+    (1, 256, 256, 1, 64, False),      # the tiny workload
+    (2, 200, 200, 3, 128, True),      # ragged tail, causal
+    (1, 77, 300, 2, 64, False),       # Nq != Nk, ragged both ways
+    (1, 300, 45, 2, 128, False),      # fewer keys than one tile
+    (1, 129, 129, 2, 64, True),
+    (2, 1, 1, 2, 128, True),          # single token
+    (1, 1, 513, 1, 128, False),       # one query, many keys
+    (1, 640, 640, 2, 128, False),
+]
+
+
+@pytest.mark.parametrize("case", DENSE_CASES, ids=lambda c: "B{}_Nq{}_Nk{}_H{}_d{}_{}".format(
+    *c[:5], "causal" if c[5] else "full"))
+def test_dense_small(case):
+    gu.need_gpu()
+    B, Nq, Nk, H, d, causal = case
+    gu.announce(f"dense {case}")
+    x = wl.make_dense(B, Nq, H, d, seed=7 + Nq + 3 * Nk + d, Nk=Nk)
+    scale = d ** -0.5
+    g = gu.run_dense(x, scale, causal)
+    r = gu.oracle_dense(x, scale, causal)
+    gu.check_forward(g["o"], g["lse"], r["o"], r["lse"], str(case))
+    gu.check_grads(g["grads"], r["grads"], str(case))
+
+
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+def test_b4_h16_n1024_d64(causal):
+    gu.need_gpu()
+    w = wl.WORKLOADS["b4_h16_n1024_d64"]
+    gu.announce(f"{w.name} causal={causal}")
+    x = wl.make_inputs(w.name)
+    g = gu.run_dense(x, w.scale, causal)
+    r = gu.oracle_dense(x, w.scale, causal)
+    gu.check_forward(g["o"], g["lse"], r["o"], r["lse"])
+    gu.check_grads(g["grads"], r["grads"])
+
+
+def test_tiny_workload():
+    gu.need_gpu()
+    w = wl.WORKLOADS["tiny"]
+    gu.announce(w.name)
+    x = wl.make_inputs(w.name)
+    g = gu.run_dense(x, w.scale, False)
+    r = gu.oracle_dense(x, w.scale, False)
+    gu.check_forward(g["o"], g["lse"], r["o"], r["lse"])
+    gu.check_grads(g["grads"], r["grads"])
+
+
+def test_scale_argument_is_used():
+    gu.need_gpu()
+    x = wl.make_dense(1, 96, 2, 64, seed=31)
+    for scale in (0.05, 0.3):
+        g = gu.run_dense(x, scale, True)
+        r = gu.oracle_dense(x, scale, True)
+        gu.check_forward(g["o"], g["lse"], r["o"], r["lse"], f"scale={scale}")
+        gu.check_grads(g["grads"], r["grads"], f"scale={scale}")
+
+
+VARLEN_CASES = [
+    # lengths_q, lengths_k (None = same), H, d, causal
+    ([1, 37, 128, 300, 0, 250], None, 4, 128, True),
+    ([64, 1, 190, 33], [100, 7, 190, 1], 2, 64, False),
+    ([513, 129], None, 2, 64, True),
+]
+
+
+@pytest.mark.parametrize("case", VARLEN_CASES, ids=lambda c: f"n{len(c[0])}_d{c[3]}_{'causal' if c[4] else 'full'}")
+def test_varlen_small(case):
+    gu.need_gpu()
+    lq, lk, H, d, causal = case
+    lk = lk or lq
+    gu.announce(f"varlen {case}")
+    scale = d ** -0.5
+    xq = wl.make_packed(lq, H, d, seed=sum(lq) + d)
+    xk = wl.make_packed(lk, H, d, seed=sum(lk) + d + 1)
+    q, do = xq["q"], xq["dout"]
+    k, v = xk["k"], xk["v"]
+    cuq, cuk = xq["cu_seqlens"], xk["cu_seqlens"]
+    dev = torch.device("cuda", 0)
+    qd, kd, vd, dod = (t.to(dev) for t in (q, k, v, do))
+    cuqd, cukd = cuq.to(dev), cuk.to(dev)
+    mq, mk = max(lq), max(lk)
+    o, lse = fa355.attention_forward_varlen(qd, kd, vd, cuqd, cukd, mq, mk, scale, causal)
+    grads = fa355.attention_backward_varlen(qd, kd, vd, o, dod, lse, cuqd, cukd, mq, mk, scale, causal)
+    torch.cuda.synchronize()
+    import oracle
+    o_ref, lse_ref = oracle.attention_forward_varlen(q, k, v, cuq, cuk, mq, scale, causal)
+    g_ref = oracle.attention_backward_varlen(q, k, v, do, cuq, cuk, scale, causal)
+    valid = ~torch.isnan(lse_ref)
+    gu.check_forward(o, lse.cpu()[valid], o_ref, lse_ref[valid], str(case))
+    gu.check_grads(grads, g_ref, str(case))
+
+
+def test_backward_is_deterministic():
+    gu.need_gpu()
+    x = wl.make_dense(2, 700, 4, 128, seed=99)
+    a = gu.run_dense(x, 128 ** -0.5, True)
+    b = gu.run_dense(x, 128 ** -0.5, True)
+    assert torch.equal(a["o"], b["o"]) and torch.equal(a["lse"], b["lse"])
+    for ga, gb in zip(a["grads"], b["grads"]):
+        assert torch.equal(ga, gb)
+
+
+def test_causal_row0_equals_v0():
+    gu.need_gpu()
+    x = wl.make_dense(2, 300, 3, 64, seed=5)
+    g = gu.run_dense(x, 0.125, True, backward=False)
+    assert torch.equal(g["o"][:, 0].cpu(), x["v"][:, 0])
+
+
+def test_outputs_fully_overwritten():
+    gu.need_gpu()
+    dev = torch.device("cuda", 0)
+    x = wl.make_dense(1, 333, 2, 128, seed=17)
+    q, k, v, do = (x[n].to(dev) for n in ("q", "k", "v", "dout"))
+    o = torch.full_like(q, float("nan"))
+    lse = torch.full((1, 2, 333), float("nan"), device=dev)
+    fa355.fa_fwd(q, k, v, o, lse, 0.1, False)
+    dq, dk, dv = (torch.full_like(t, float("nan")) for t in (q, k, v))
+    ws = torch.full((fa355.fa_bwd_workspace_bytes(1, 2, 333, 128) // 4,), float("nan"), device=dev)
+    fa355.fa_bwd(q, k, v, o, do, lse, dq, dk, dv, ws, 0.1, False)
+    torch.cuda.synchronize()
+    for t in (o, lse, dq, dk, dv):
+        assert torch.isfinite(t).all()
