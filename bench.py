@@ -1,0 +1,192 @@
+"""Benchmark: exact attention forward + backward on one MI355X.
+
+One step = the whole hot path on the headline workload (B8 H16 N4096 d128,
+causal, bf16): fa_fwd, then the backward's three stages (fa_bwd_dot,
+fa_bwd_dkdv, fa_bwd_dq), all on one stream with inputs resident in HBM.
+W untimed warm-up steps, then exactly K timed steps bracketed by device
+synchronisation; HIP events around each kernel give per-kernel durations.
+
+Prints ONE JSON line.  `value` is fwd+bwd algorithmic TFLOP/s (4d + 10d FLOPs per
+(query, key) pair; causal pairs = N(N+1)/2).  `roofline` describes the kernel that
+takes the most time per step; `cpu_baseline` times the CPU fp64 oracle on a
+time-bounded sample of the same workload's heads.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import torch
+
+from io_aware_exact_attention_amd import accounting as acc
+from io_aware_exact_attention_amd import fa355
+from io_aware_exact_attention_amd import workloads as wl
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+METRIC = "attention fwd & fwd+bwd TFLOP/s, % bf16 MFMA peak, B8 H16 N4096 d128 causal"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=wl.HEADLINE)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="wall-time budget of the CPU oracle sample (0 disables it)")
+    return ap.parse_args()
+
+
+def cpu_baseline(x, w, causal, budget_s: float):
+    """Time the fp64 oracle, fwd + bwd, head by head until the budget is used."""
+    import oracle   # test infrastructure: only this leg of the benchmark uses it
+
+    cores = len(os.sched_getaffinity(0))
+    torch.set_num_threads(cores)
+    B, N, H, d = x["q"].shape
+    done, flops, t_total = 0, 0, 0.0
+    for b in range(B):
+        for h in range(H):
+            sl = (slice(b, b + 1), slice(None), slice(h, h + 1))
+            q, k, v, do = (x[n][sl].contiguous() for n in ("q", "k", "v", "dout"))
+            t0 = time.perf_counter()
+            oracle.attention_forward(q, k, v, w.scale, causal)
+            oracle.attention_backward(q, k, v, do, w.scale, causal)
+            t_total += time.perf_counter() - t0
+            done += 1
+            p = acc.pairs(N, N, causal)
+            flops += acc.flops_fwd(p, d) + acc.flops_bwd(p, d)
+            if t_total >= budget_s:
+                break
+        if t_total >= budget_s:
+            break
+    return {
+        "value": round(flops / t_total / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": torch.get_num_threads(),
+        "kind": "oracle",
+        "sample": f"{done} of {B * H} (batch, head) slices, forward + backward, float64, "
+                  f"{t_total:.1f} s",
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(heads and batch entries are independent, see the design notes)", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    w = wl.WORKLOADS[args.workload]
+    if w.varlen:
+        raise SystemExit("bench.py times the dense workloads")
+    causal = w.causal[-1]
+    dev = torch.device("cuda", 0)
+    x = wl.make_inputs(w.name)
+    q, k, v, do = (x[n].to(dev) for n in ("q", "k", "v", "dout"))
+    B, N, H, d = q.shape
+    o = torch.empty_like(q)
+    lse = torch.empty(B, H, N, dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dvec = torch.empty(B, H, N, dtype=torch.float32, device=dev)
+    scale = w.scale
+
+    names = ["fa_fwd_kernel", "fa_bwd_dot_kernel", "fa_bwd_dkdv_kernel", "fa_bwd_dq_kernel"]
+    calls = [
+        lambda: fa355.fa_fwd(q, k, v, o, lse, scale, causal),
+        lambda: fa355.fa_bwd_dot(o, do, dvec),
+        lambda: fa355.fa_bwd_dkdv(q, k, v, do, lse, dvec, dk, dv, scale, causal),
+        lambda: fa355.fa_bwd_dq(q, k, v, do, lse, dvec, dq, scale, causal),
+    ]
+    for _ in range(args.warmup):
+        for c in calls:
+            c()
+    torch.cuda.synchronize()
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)]
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        ev[s][0].record()
+        for i, c in enumerate(calls):
+            c()
+            ev[s][i + 1].record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / args.steps
+    kern_ms = [sum(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(args.steps)) / args.steps
+               for i in range(len(calls))]
+
+    cnt = acc.dense_counts(B, H, N, d, causal)
+    pairs = cnt["pairs"]
+    f_fwd, f_bwd = cnt["flops_fwd"], cnt["flops_bwd"]
+    # algorithmic FLOPs / bytes attributed per kernel (the 10d backward = 8d in dK/dV + 2d in dQ)
+    kern_flops = [f_fwd, 0, 8 * d * pairs, 2 * d * pairs]
+    dot_bytes = B * N * H * (2 * 2 * d + 4)
+    kern = {}
+    for n, ms, fl in zip(names, kern_ms, kern_flops):
+        e = {"ms": round(ms, 4)}
+        if fl:
+            e["tflops"] = round(fl / (ms * 1e-3) / 1e12, 2)
+        else:
+            e["gbs"] = round(dot_bytes / (ms * 1e-3) / 1e9, 1)
+        kern[n] = e
+    dom = max(range(len(names)), key=lambda i: kern_ms[i])
+    if kern_flops[dom]:
+        achieved = kern_flops[dom] / (kern_ms[dom] * 1e-3) / 1e12
+        roof = {"kernel": names[dom], "bound": "mfma", "achieved": round(achieved, 2),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None}
+    else:
+        achieved = dot_bytes / (kern_ms[dom] * 1e-3) / 1e9
+        roof = {"kernel": names[dom], "bound": "hbm", "achieved": round(achieved, 1),
+                "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                "traffic": None}
+
+    t_fwd = kern_ms[0]
+    t_bwd = sum(kern_ms[1:])
+    fwd_tf = f_fwd / (t_fwd * 1e-3) / 1e12
+    fb_tf_events = (f_fwd + f_bwd) / ((t_fwd + t_bwd) * 1e-3) / 1e12
+    value = (f_fwd + f_bwd) / wall / 1e12
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": B, "H": H, "N": N, "d": d, "causal": causal,
+                   "scale": scale},
+        "fwd_tflops": round(fwd_tf, 2),
+        "fwd_pct_peak": round(100 * fwd_tf / PEAK_BF16_TFLOPS, 2),
+        "fwd_bwd_tflops_kernels": round(fb_tf_events, 2),
+        "fwd_bwd_pct_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "fwd_hbm_gbs": round(cnt["bytes_fwd"] / (t_fwd * 1e-3) / 1e9, 1),
+        "kernels": kern,
+        "roofline": roof,
+        "device": torch.cuda.get_device_name(0),
+    }
+    if args.cpu_seconds > 0:
+        xc = {n: x[n] for n in ("q", "k", "v", "dout")}
+        out["cpu_baseline"] = cpu_baseline(xc, w, causal, args.cpu_seconds)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

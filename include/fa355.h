@@ -109,6 +109,24 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
            size_t workspace_bytes, int B, int H, int Nq, int Nk, int d, float scale,
            int causal, void* stream);
 
+/*
+ * The three stages fa_bwd runs, exposed separately (dense batch only) for callers
+ * that time them or need only some gradients.  Arguments mean what they mean in
+ * fa_bwd; `dvec` is the fp32 row vector D [B,H,Nq] (fa_bwd's workspace).
+ *   fa_bwd_dot:  D_i = sum_c dO_ic * O_ic                    (writes dvec)
+ *   fa_bwd_dkdv: dK, dV from q, k, v, dout, lse, dvec         (writes dk, dv)
+ *   fa_bwd_dq:   dQ from q, k, v, dout, lse, dvec             (writes dq)
+ * fa_bwd_dkdv and fa_bwd_dq both need dvec from fa_bwd_dot on the same stream.
+ */
+int fa_bwd_dot(const void* o, const void* dout, float* dvec, int B, int H, int Nq, int d,
+               void* stream);
+int fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, const float* lse,
+                const float* dvec, void* dk, void* dv, int B, int H, int Nq, int Nk, int d,
+                float scale, int causal, void* stream);
+int fa_bwd_dq(const void* q, const void* k, const void* v, const void* dout, const float* lse,
+              const float* dvec, void* dq, int B, int H, int Nq, int Nk, int d, float scale,
+              int causal, void* stream);
+
 /* Backward, packed variable-length batch; arguments as fa_fwd_varlen and fa_bwd. */
 int fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o,
                   const void* dout, const float* lse, void* dq, void* dk, void* dv,

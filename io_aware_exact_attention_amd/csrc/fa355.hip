@@ -87,43 +87,46 @@ int launch_fwd(const AttnParams& p, int d, int causal, hipStream_t s) {
     return d == 64 ? launch_fwd_d<64, VARLEN>(p, causal, s) : launch_fwd_d<128, VARLEN>(p, causal, s);
 }
 
+// Backward stages.  `p.n_tiles` is set per stage from the stage's own tiling.
 template <int D, bool VARLEN>
-int launch_bwd_d(AttnParams p, int causal, hipStream_t s) {
+int launch_bwd_dot_d(AttnParams p, hipStream_t s) {
     using Pre = BwdPreCfg<D>;
-    using KV = BwdKVCfg<D>;
-    using Q = BwdQCfg<D>;
-    int st;
-    // 1) D_i = rowsum(dO * O)
-    {
-        AttnParams pp = p;
-        pp.n_tiles = (p.nq + Pre::ROWS - 1) / Pre::ROWS;
-        const int grid = pp.n_tiles * p.H * p.batch;
-        st = launch(fa_bwd_dot_kernel<D, VARLEN>, grid, Pre::THREADS, s, pp);
-        if (st) return st;
-    }
-    // 2) dK, dV: one work-group per key tile, no atomics
-    {
-        AttnParams pk = p;
-        pk.n_tiles = (p.nk + KV::BN - 1) / KV::BN;
-        const int grid = pk.n_tiles * p.H * p.batch;
-        st = causal ? launch(fa_bwd_dkdv_kernel<D, true, VARLEN>, grid, KV::NW * 64, s, pk)
-                    : launch(fa_bwd_dkdv_kernel<D, false, VARLEN>, grid, KV::NW * 64, s, pk);
-        if (st) return st;
-    }
-    // 3) dQ: one work-group per query tile, no atomics
-    {
-        AttnParams pq = p;
-        pq.n_tiles = (p.nq + Q::BM - 1) / Q::BM;
-        const int grid = pq.n_tiles * p.H * p.batch;
-        st = causal ? launch(fa_bwd_dq_kernel<D, true, VARLEN>, grid, Q::NW * 64, s, pq)
-                    : launch(fa_bwd_dq_kernel<D, false, VARLEN>, grid, Q::NW * 64, s, pq);
-    }
-    return st;
+    p.n_tiles = (p.nq + Pre::ROWS - 1) / Pre::ROWS;
+    return launch(fa_bwd_dot_kernel<D, VARLEN>, p.n_tiles * p.H * p.batch, Pre::THREADS, s, p);
 }
 
+template <int D, bool VARLEN>
+int launch_bwd_dkdv_d(AttnParams p, int causal, hipStream_t s) {
+    using KV = BwdKVCfg<D>;
+    p.n_tiles = (p.nk + KV::BN - 1) / KV::BN;
+    const int grid = p.n_tiles * p.H * p.batch;
+    return causal ? launch(fa_bwd_dkdv_kernel<D, true, VARLEN>, grid, KV::NW * 64, s, p)
+                  : launch(fa_bwd_dkdv_kernel<D, false, VARLEN>, grid, KV::NW * 64, s, p);
+}
+
+template <int D, bool VARLEN>
+int launch_bwd_dq_d(AttnParams p, int causal, hipStream_t s) {
+    using Q = BwdQCfg<D>;
+    p.n_tiles = (p.nq + Q::BM - 1) / Q::BM;
+    const int grid = p.n_tiles * p.H * p.batch;
+    return causal ? launch(fa_bwd_dq_kernel<D, true, VARLEN>, grid, Q::NW * 64, s, p)
+                  : launch(fa_bwd_dq_kernel<D, false, VARLEN>, grid, Q::NW * 64, s, p);
+}
+
+enum BwdStage { kStageDot = 1, kStageDkdv = 2, kStageDq = 4, kStageAll = 7 };
+
 template <bool VARLEN>
-int launch_bwd(const AttnParams& p, int d, int causal, hipStream_t s) {
-    return d == 64 ? launch_bwd_d<64, VARLEN>(p, causal, s) : launch_bwd_d<128, VARLEN>(p, causal, s);
+int launch_bwd(const AttnParams& p, int d, int causal, hipStream_t s, int stages = kStageAll) {
+    int st = FA_OK;
+    if (stages & kStageDot)
+        st = d == 64 ? launch_bwd_dot_d<64, VARLEN>(p, s) : launch_bwd_dot_d<128, VARLEN>(p, s);
+    if (!st && (stages & kStageDkdv))
+        st = d == 64 ? launch_bwd_dkdv_d<64, VARLEN>(p, causal, s)
+                     : launch_bwd_dkdv_d<128, VARLEN>(p, causal, s);
+    if (!st && (stages & kStageDq))
+        st = d == 64 ? launch_bwd_dq_d<64, VARLEN>(p, causal, s)
+                     : launch_bwd_dq_d<128, VARLEN>(p, causal, s);
+    return st;
 }
 
 AttnParams base_params(const void* q, const void* k, const void* v, int batch, int H, int nq,
@@ -239,6 +242,62 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
     p.dv = static_cast<bf16*>(dv);
     p.dvec = static_cast<float*>(workspace);
     return launch_bwd<false>(p, d, causal, static_cast<hipStream_t>(stream));
+}
+
+int fa_bwd_dot(const void* o, const void* dout, float* dvec, int B, int H, int Nq, int d,
+               void* stream) {
+    if (!o || !dout || !dvec) return FA_ERR_NULL;
+    if (B <= 0 || Nq <= 0) return FA_ERR_SHAPE;
+    int st = check_common(H, d, 1.f, 0);
+    if (st) return st;
+    if (!aligned(o, 16) || !aligned(dout, 16) || !aligned(dvec, 4)) return FA_ERR_ALIGN;
+    st = check_sizes((int64_t)B * Nq, (int64_t)B * Nq, H, d, (int64_t)((Nq + 15) / 16) * H * B);
+    if (st) return st;
+    AttnParams p = base_params(nullptr, nullptr, nullptr, B, H, Nq, Nq, 1.f);
+    p.o_in = static_cast<const bf16*>(o);
+    p.dout = static_cast<const bf16*>(dout);
+    p.dvec = dvec;
+    return launch_bwd<false>(p, d, 0, static_cast<hipStream_t>(stream), kStageDot);
+}
+
+static int bwd_stage(int stage, const void* q, const void* k, const void* v, const void* dout,
+                     const float* lse, const float* dvec, void* dq, void* dk, void* dv, int B, int H,
+                     int Nq, int Nk, int d, float scale, int causal, void* stream) {
+    if (!q || !k || !v || !dout || !lse || !dvec) return FA_ERR_NULL;
+    if (stage == kStageDkdv && (!dk || !dv)) return FA_ERR_NULL;
+    if (stage == kStageDq && !dq) return FA_ERR_NULL;
+    if (B <= 0 || Nq <= 0 || Nk <= 0) return FA_ERR_SHAPE;
+    int st = check_common(H, d, scale, causal);
+    if (st) return st;
+    if (causal && Nq != Nk) return FA_ERR_UNSUPPORTED;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(dout, 16) ||
+        !aligned(lse, 4) || !aligned(dvec, 4) || (dq && !aligned(dq, 16)) ||
+        (dk && !aligned(dk, 16)) || (dv && !aligned(dv, 16)))
+        return FA_ERR_ALIGN;
+    st = check_sizes((int64_t)B * Nq, (int64_t)B * Nk, H, d, (int64_t)((Nq + 15) / 16) * H * B);
+    if (st) return st;
+    AttnParams p = base_params(q, k, v, B, H, Nq, Nk, scale);
+    p.dout = static_cast<const bf16*>(dout);
+    p.lse_in = lse;
+    p.dvec = const_cast<float*>(dvec);
+    p.dq = static_cast<bf16*>(dq);
+    p.dk = static_cast<bf16*>(dk);
+    p.dv = static_cast<bf16*>(dv);
+    return launch_bwd<false>(p, d, causal, static_cast<hipStream_t>(stream), stage);
+}
+
+int fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, const float* lse,
+                const float* dvec, void* dk, void* dv, int B, int H, int Nq, int Nk, int d,
+                float scale, int causal, void* stream) {
+    return bwd_stage(kStageDkdv, q, k, v, dout, lse, dvec, nullptr, dk, dv, B, H, Nq, Nk, d, scale,
+                     causal, stream);
+}
+
+int fa_bwd_dq(const void* q, const void* k, const void* v, const void* dout, const float* lse,
+              const float* dvec, void* dq, int B, int H, int Nq, int Nk, int d, float scale,
+              int causal, void* stream) {
+    return bwd_stage(kStageDq, q, k, v, dout, lse, dvec, dq, nullptr, nullptr, B, H, Nq, Nk, d, scale,
+                     causal, stream);
 }
 
 int fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o, const void* dout,

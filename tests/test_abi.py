@@ -91,6 +91,18 @@ def test_varlen_rejects():
     assert lib.fa_bwd_varlen(*[A] * 9, A, 1 << 20, None, A, 2, 16, 16, 1, 64, 0.1, 0, None) == -1
 
 
+def test_stage_entry_points_reject():
+    lib = fa355.lib()
+    assert lib.fa_bwd_dot(None, A, A, 1, 1, 16, 64, None) == -1
+    assert lib.fa_bwd_dot(A, A, A, 1, 1, 16, 72, None) == -3
+    assert lib.fa_bwd_dot(A, MIS, A, 1, 1, 16, 64, None) == -4
+    assert lib.fa_bwd_dkdv(*[A] * 6, None, A, 1, 1, 16, 16, 64, 0.1, 0, None) == -1
+    assert lib.fa_bwd_dkdv(*[A] * 8, 1, 1, 16, 8, 64, 0.1, 1, None) == -3
+    assert lib.fa_bwd_dq(*[A] * 6, None, 1, 1, 16, 16, 64, 0.1, 0, None) == -1
+    assert lib.fa_bwd_dq(*[A] * 6, MIS, 1, 1, 16, 16, 64, 0.1, 0, None) == -4
+    assert lib.fa_bwd_dq(*[A] * 7, 1, 1, 0, 16, 64, 0.1, 0, None) == -2
+
+
 def test_binding_raises_on_error():
     with pytest.raises(fa355.FaError) as e:
         fa355._check(-3)
