@@ -29,6 +29,8 @@ from io_aware_exact_attention_amd import workloads as wl
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
+CALIB_BYTES = 256 << 20     # size of the counter-calibration copy
+
 METRIC = "attention fwd & fwd+bwd TFLOP/s, % bf16 MFMA peak, B8 H16 N4096 d128 causal"
 
 
@@ -106,6 +108,14 @@ def main():
         lambda: fa355.fa_bwd_dkdv(q, k, v, do, lse, dvec, dk, dv, scale, causal),
         lambda: fa355.fa_bwd_dq(q, k, v, do, lse, dvec, dq, scale, causal),
     ]
+    # One plain device copy of known size, outside the timed region: under
+    # rocprofv3 --pmc its FETCH_SIZE / WRITE_SIZE calibrate the byte counters.
+    calib = torch.empty(CALIB_BYTES // 2, dtype=torch.bfloat16, device=dev)
+    calib_dst = torch.empty_like(calib)
+    calib_dst.copy_(calib)
+    del calib, calib_dst
+    torch.cuda.synchronize()
+
     for _ in range(args.warmup):
         for c in calls:
             c()

@@ -6,15 +6,18 @@
 namespace fa355 {
 
 // LDS tiles are row-major [row][D] bf16 with the 16-byte chunks of each row
-// permuted: logical chunk c of row r sits at physical chunk c ^ tile_swz(r).  The
-// XOR keeps 32-byte segments' halves adjacent except on odd XOR values, and is
-// chosen so that (a) 16 consecutive rows read at one logical chunk (row-wise
-// operand reads, ds_read_b128) and (b) 8 consecutive rows read at two adjacent
-// chunks (transposed operand reads, ds_read_b64_tr_b16) all hit distinct banks.
+// permuted: logical chunk c of row r sits at physical chunk c ^ tile_swz(r).
+// Measured on gfx950 (bank-conflict counter), the LDS serves a ds_read_b128 in
+// groups of 16 lanes and a ds_read_b64_tr_b16 in groups of 32 lanes, each group
+// conflict-free when it touches 256 distinct bytes modulo 256.  The kernels read
+// (a) 16 consecutive rows at one logical chunk (row-wise operands) and (b) 4
+// consecutive rows (from a multiple of 4) at 4 adjacent chunks, 64 bytes each
+// (transposed operands).  The XOR below makes (a) a permutation of the 16 chunk
+// slots and sends the 4 rows of (b) to 4 different 64-byte bank groups.
 template <int D>
 __device__ __forceinline__ int tile_swz(int row) {
-    if constexpr (D == 128) return 2 * (row & 7) + ((row >> 3) & 1);
-    else return 2 * ((row >> 1) & 3) + ((row >> 3) & 1);
+    if constexpr (D == 128) return 4 * (row & 3) + ((row >> 2) & 3);
+    else return 4 * ((row >> 1) & 1) + ((row >> 2) & 3);   // 128-byte rows: 2 per 256 bytes
 }
 
 // Byte offset of the 16-byte chunk holding logical chunk `chunk` of `row`.
