@@ -51,7 +51,8 @@ typedef enum fa_status {
     FA_OK = 0,
     FA_ERR_NULL = -1,        /* a required pointer is NULL                         */
     FA_ERR_SHAPE = -2,       /* a size is <= 0, or sizes are inconsistent/too big   */
-    FA_ERR_UNSUPPORTED = -3, /* d not in {64,128}, causal with Nq != Nk, bad scale  */
+    FA_ERR_UNSUPPORTED = -3, /* d not in {64,128}, causal with Nq != Nk, bad scale,
+                                one sequence's rows of a tensor >= 2 GiB */
     FA_ERR_ALIGN = -4,       /* a tensor pointer is not 16-byte (fp32: 4-byte) aligned */
     FA_ERR_LAUNCH = -5,      /* the HIP runtime rejected a kernel launch            */
     FA_ERR_WORKSPACE = -6    /* workspace missing or smaller than required          */

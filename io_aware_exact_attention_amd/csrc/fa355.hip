@@ -34,9 +34,15 @@ int check_common(int H, int d, float scale, int causal) {
 }
 
 // tokens * H * d elements must be addressable; grid sizes must fit an int.
-int check_sizes(int64_t tokens_q, int64_t tokens_k, int H, int d, int64_t grid) {
+// seq_q / seq_k: rows of one sequence.  The kernels address one sequence's
+// rows of one tensor through a buffer resource with a 32-bit signed range, so
+// seq * H * d * 2 bytes must stay below 2 GiB.
+int check_sizes(int64_t tokens_q, int64_t tokens_k, int64_t seq_q, int64_t seq_k, int H, int d,
+                int64_t grid) {
     const int64_t lim = (int64_t)1 << 40;
+    const int64_t span = (int64_t)1 << 31;
     if (tokens_q <= 0 || tokens_k <= 0) return FA_ERR_SHAPE;
+    if (seq_q * H * d * 2 >= span || seq_k * H * d * 2 >= span) return FA_ERR_UNSUPPORTED;
     if (tokens_q > INT_MAX || tokens_k > INT_MAX) return FA_ERR_SHAPE;
     if (tokens_q * H * d > lim || tokens_k * H * d > lim) return FA_ERR_SHAPE;
     if (grid <= 0 || grid > INT_MAX) return FA_ERR_SHAPE;
@@ -78,8 +84,9 @@ int launch(K kernel, int grid, int block, hipStream_t s, const AttnParams& p) {
 template <int D, bool VARLEN>
 int launch_fwd_d(const AttnParams& p, int causal, hipStream_t s) {
     const int grid = p.n_tiles * p.H * p.batch;
-    return causal ? launch(fa_fwd_kernel<D, true, VARLEN>, grid, 256, s, p)
-                  : launch(fa_fwd_kernel<D, false, VARLEN>, grid, 256, s, p);
+    const int block = FwdCfg<D>::NW * 64;
+    return causal ? launch(fa_fwd_kernel<D, true, VARLEN>, grid, block, s, p)
+                  : launch(fa_fwd_kernel<D, false, VARLEN>, grid, block, s, p);
 }
 
 template <bool VARLEN>
@@ -173,8 +180,8 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
     if (causal && Nq != Nk) return FA_ERR_UNSUPPORTED;
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
         return FA_ERR_ALIGN;
-    const int ntq = (Nq + 127) / 128;
-    st = check_sizes((int64_t)B * Nq, (int64_t)B * Nk, H, d, (int64_t)ntq * H * B);
+    const int ntq = (Nq + FwdCfg<128>::BM - 1) / FwdCfg<128>::BM;
+    st = check_sizes((int64_t)B * Nq, (int64_t)B * Nk, Nq, Nk, H, d, (int64_t)ntq * H * B);
     if (st) return st;
     AttnParams p = base_params(q, k, v, B, H, Nq, Nk, scale);
     p.o = static_cast<bf16*>(o);
@@ -193,8 +200,9 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* l
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4) ||
         !aligned(cu_seqlens_q, 4) || !aligned(cu_seqlens_k, 4))
         return FA_ERR_ALIGN;
-    const int ntq = (max_seqlen_q + 127) / 128;
-    st = check_sizes((int64_t)nseq * max_seqlen_q, (int64_t)nseq * max_seqlen_k, H, d,
+    const int ntq = (max_seqlen_q + FwdCfg<128>::BM - 1) / FwdCfg<128>::BM;
+    st = check_sizes((int64_t)nseq * max_seqlen_q, (int64_t)nseq * max_seqlen_k, max_seqlen_q,
+                     max_seqlen_k, H, d,
                      (int64_t)ntq * H * nseq);
     if (st) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -231,7 +239,7 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
         !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(lse, 4) ||
         !aligned(workspace, 4))
         return FA_ERR_ALIGN;
-    st = check_sizes((int64_t)B * Nq, (int64_t)B * Nk, H, d, (int64_t)((Nq + 15) / 16) * H * B);
+    st = check_sizes((int64_t)B * Nq, (int64_t)B * Nk, Nq, Nk, H, d, (int64_t)((Nq + 15) / 16) * H * B);
     if (st) return st;
     AttnParams p = base_params(q, k, v, B, H, Nq, Nk, scale);
     p.o_in = static_cast<const bf16*>(o);
@@ -251,7 +259,7 @@ int fa_bwd_dot(const void* o, const void* dout, float* dvec, int B, int H, int N
     int st = check_common(H, d, 1.f, 0);
     if (st) return st;
     if (!aligned(o, 16) || !aligned(dout, 16) || !aligned(dvec, 4)) return FA_ERR_ALIGN;
-    st = check_sizes((int64_t)B * Nq, (int64_t)B * Nq, H, d, (int64_t)((Nq + 15) / 16) * H * B);
+    st = check_sizes((int64_t)B * Nq, (int64_t)B * Nq, Nq, Nq, H, d, (int64_t)((Nq + 15) / 16) * H * B);
     if (st) return st;
     AttnParams p = base_params(nullptr, nullptr, nullptr, B, H, Nq, Nq, 1.f);
     p.o_in = static_cast<const bf16*>(o);
@@ -274,7 +282,7 @@ static int bwd_stage(int stage, const void* q, const void* k, const void* v, con
         !aligned(lse, 4) || !aligned(dvec, 4) || (dq && !aligned(dq, 16)) ||
         (dk && !aligned(dk, 16)) || (dv && !aligned(dv, 16)))
         return FA_ERR_ALIGN;
-    st = check_sizes((int64_t)B * Nq, (int64_t)B * Nk, H, d, (int64_t)((Nq + 15) / 16) * H * B);
+    st = check_sizes((int64_t)B * Nq, (int64_t)B * Nk, Nq, Nk, H, d, (int64_t)((Nq + 15) / 16) * H * B);
     if (st) return st;
     AttnParams p = base_params(q, k, v, B, H, Nq, Nk, scale);
     p.dout = static_cast<const bf16*>(dout);
@@ -316,7 +324,8 @@ int fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o, co
         !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(lse, 4) ||
         !aligned(workspace, 4) || !aligned(cu_seqlens_q, 4) || !aligned(cu_seqlens_k, 4))
         return FA_ERR_ALIGN;
-    st = check_sizes((int64_t)nseq * max_seqlen_q, (int64_t)nseq * max_seqlen_k, H, d,
+    st = check_sizes((int64_t)nseq * max_seqlen_q, (int64_t)nseq * max_seqlen_k, max_seqlen_q,
+                     max_seqlen_k, H, d,
                      (int64_t)((max_seqlen_q + 15) / 16) * H * nseq);
     if (st) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);

@@ -70,6 +70,11 @@ void fa_fwd_kernel(AttnParams p) {
     const int64_t tok = (int64_t)p.H * D;
     const bf16* kbase = p.k + (int64_t)ks * tok + h * D;
     const bf16* vbase = p.v + (int64_t)ks * tok + h * D;
+    const int row_bytes = p.H * D * 2;
+    const uint32_t kv_bytes = (uint32_t)nk * row_bytes;
+    const TileLoader<D, C::BN, C::NW> loader(row_bytes, wave, lane);
+    FA_LDS char* ldsb = (FA_LDS char*)smem;
+    const int wave_s = __builtin_amdgcn_readfirstlane(wave);   // LDS destinations are wave-uniform
 
     const int qw0 = q_start + wave * 32;   // first query row of this wave
     const int qi = qw0 + col;              // this lane's query row
@@ -88,8 +93,8 @@ void fa_fwd_kernel(AttnParams p) {
     const float c = p.scale_log2;
 
     if (n_kv > 0) {
-        load_tile_lds<D, C::BN, C::NW>(smem, kbase, tok, 0, nk, wave, lane);
-        load_tile_lds<D, C::BN, C::NW>(smem + C::TILE_BYTES, vbase, tok, 0, nk, wave, lane);
+        loader.load(ldsb, kbase, kv_bytes, 0, wave_s);
+        loader.load(ldsb + C::TILE_BYTES, vbase, kv_bytes, 0, wave_s);
     }
     for (int t = 0; t < n_kv; ++t) {
         char* kt = smem + (t & 1) * 2 * C::TILE_BYTES;
@@ -97,10 +102,9 @@ void fa_fwd_kernel(AttnParams p) {
         wait_vmem();
         __syncthreads();
         if (t + 1 < n_kv) {
-            char* kn = smem + ((t + 1) & 1) * 2 * C::TILE_BYTES;
-            load_tile_lds<D, C::BN, C::NW>(kn, kbase, tok, (t + 1) * C::BN, nk, wave, lane);
-            load_tile_lds<D, C::BN, C::NW>(kn + C::TILE_BYTES, vbase, tok, (t + 1) * C::BN, nk,
-                                                 wave, lane);
+            FA_LDS char* kn = ldsb + ((t + 1) & 1) * 2 * C::TILE_BYTES;
+            loader.load(kn, kbase, kv_bytes, (t + 1) * C::BN * row_bytes, wave_s);
+            loader.load(kn + C::TILE_BYTES, vbase, kv_bytes, (t + 1) * C::BN * row_bytes, wave_s);
         }
         const int kv0 = t * C::BN;
         if (CAUSAL && kv0 > qw0 + 31) continue;   // every key here is above this wave's rows

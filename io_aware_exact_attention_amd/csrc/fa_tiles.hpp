@@ -61,4 +61,45 @@ __device__ __forceinline__ bool wave_any(bool pred) {
     return __builtin_amdgcn_ballot_w64(pred) != 0;
 }
 
+// Per-lane byte offsets for streaming a [ROWS x D] bf16 tile (rows `row_bytes`
+// apart in memory) into LDS with 16-byte buffer loads: instruction i of wave w
+// writes the 1 KB LDS slice (w * INSTS + i) of the swizzled tile, lane l's 16
+// bytes landing at slice + 16 l.
+template <int D, int ROWS, int NW>
+struct TileLoader {
+    static constexpr int CPR = D / 8;
+    static constexpr int ROWS_PER_INST = 1024 / (D * 2);
+    static constexpr int INSTS = ROWS * D * 2 / 1024 / NW;
+    static_assert(ROWS * D * 2 % (1024 * NW) == 0, "tile must split evenly over waves");
+    int voff[INSTS];
+
+    __device__ __forceinline__ TileLoader(int row_bytes, int wave, int lane) {
+#pragma unroll
+        for (int i = 0; i < INSTS; ++i) {
+            const int r = (wave * INSTS + i) * ROWS_PER_INST + lane / CPR;
+            const int lc = (lane % CPR) ^ tile_swz<D>(r);   // logical chunk stored in this slot
+            voff[i] = r * row_bytes + 16 * lc;
+        }
+    }
+
+    // Rows [first, first + ROWS) of the tensor starting at `base`, whose valid
+    // rows span `bytes` bytes; `first_bytes` = first * row_bytes (wave-uniform).
+    // The loads go through a raw buffer resource (gfx9-family word 3) whose range
+    // ends at `bytes`: rows past it read as zeros and touch no memory.
+    __device__ __forceinline__ void load(FA_LDS char* lds_tile, const void* base, uint32_t bytes,
+                                         int first_bytes, int wave) const {
+#if defined(__HIP_DEVICE_COMPILE__)
+        // (the resource type exists only for the device; keeping it out of the
+        // host pass also keeps clang emitting every kernel instantiation's stub)
+        const auto rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
+                                                            (int)bytes, 0x00020000);
+#pragma unroll
+        for (int i = 0; i < INSTS; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rsrc, (FA_LDS void*)(lds_tile + (wave * INSTS + i) * 1024), 16, voff[i],
+                first_bytes, 0, 0);
+#endif
+    }
+};
+
 }  // namespace fa355

@@ -63,6 +63,8 @@ def test_fwd_null(arg):
     (dict(scale=0.0), -3), (dict(scale=float("nan")), -3), (dict(scale=float("inf")), -3),
     (dict(q=MIS), -4), (dict(o=MIS), -4), (dict(lse=A + 2), -4),
     (dict(B=1 << 20, Nq=1 << 20, Nk=1 << 20), -2),
+    # one sequence's key rows of one tensor span 4 GiB: beyond a buffer range
+    (dict(H=16, Nq=1 << 20, Nk=1 << 20, d=128), -3),
 ])
 def test_fwd_rejects(kw, code):
     assert _fwd(**kw) == code
@@ -77,6 +79,7 @@ def test_bwd_rejects():
     assert _bwd(ptrs=[A] * 6 + [MIS] + [A] * 2) == -4
     assert _bwd(ws=A + 2) == -4
     assert _bwd(Nq=0) == -2
+    assert _bwd(H=16, Nq=1 << 20, Nk=1 << 20, d=128, wsb=1 << 40) == -3
 
 
 def test_varlen_rejects():
