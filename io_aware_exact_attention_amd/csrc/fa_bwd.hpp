@@ -10,11 +10,12 @@
 // Three kernels, all stream-ordered and free of atomics (every output element
 // is owned by exactly one work-group, so results are bitwise deterministic):
 //   1. fa_bwd_dot_kernel:  D_i = rowsum(dO * O), one pass over O and dO.
-//   2. fa_bwd_dkdv_kernel: key-tile outer.  A work-group keeps a 128-key tile of
-//      K and V in registers (32 keys per wave) and the dK^T, dV^T accumulators on
-//      chip, streams the query tiles that can see those keys (Q, dO, LSE, D;
-//      double-buffered through LDS) and evaluates S, dP (row-wise LDS operand
-//      reads) and dV^T += dO^T P, dK^T += Q^T dS (transposed LDS operand reads).
+//   2. fa_bwd_dkdv_kernel: key-tile outer.  A work-group owns a 128-key tile
+//      (K rows in registers, 32 keys per wave; V in LDS) and keeps the dK^T,
+//      dV^T accumulators on chip, streams the query rows that can see those keys
+//      (Q, dO, LSE, D; double-buffered through LDS) and evaluates S, dP
+//      (row-wise LDS operand reads) and dV^T += dO^T P, dK^T += Q^T dS
+//      (transposed LDS operand reads).
 //      S = Q K^T is computed with keys as the accumulator's columns, so each
 //      lane's P / dS registers are directly the B operand of those products.
 //   3. fa_bwd_dq_kernel: query-tile outer, the forward's structure: Q and dO rows
@@ -39,12 +40,15 @@ template <int D>
 struct BwdKVCfg {
     static constexpr int NW = 4;
     static constexpr int BN = 32 * NW;            // keys per work-group (32 per wave)
-    static constexpr int BMQ = 64;                // query rows per streamed stage
+    static constexpr int BMQ = 32;                // query rows per streamed stage
     static constexpr int ROW_BYTES = D * 2;
     static constexpr int TILE_BYTES = BMQ * ROW_BYTES;
-    static constexpr int STAT_BYTES = 2 * BMQ * 4;   // LSE then D, fp32
-    static constexpr int STAGE_BYTES = 2 * TILE_BYTES + STAT_BYTES;
-    static constexpr int LDS_BYTES = 2 * STAGE_BYTES;
+    static constexpr int V_BYTES = BN * ROW_BYTES;
+    static constexpr int STAT_BYTES = 512;        // 64 LSE then 64 D values, fp32
+    // [V tile][Q | dO stage 0][Q | dO stage 1][stats 0][stats 1]
+    static constexpr int STAGE0 = V_BYTES;
+    static constexpr int STATS0 = V_BYTES + 4 * TILE_BYTES;
+    static constexpr int LDS_BYTES = STATS0 + 2 * STAT_BYTES;
     static constexpr int KSTEPS = D / 16;
     static constexpr int DBLK = D / 32;
 };
@@ -88,23 +92,23 @@ __global__ __launch_bounds__(256) void fa_bwd_dot_kernel(AttnParams p) {
     if (c8 == 0 && r < nq) p.dvec[((int64_t)b * p.H + h) * p.nq + r] = acc;
 }
 
-// One fp32 per lane: rows [r0, r0 + 64) of a per-row vector into LDS.
-__device__ __forceinline__ void load_row_stats(char* lds, const float* base, int r0, int nrows,
-                                               int lane) {
-    const int row = min(r0 + lane, nrows - 1);
-    __builtin_amdgcn_global_load_lds(base + row, (FA_LDS void*)lds, 4, 0, 0);
-}
-
 // ---------------------------------------------------------------------------
 // 2. dK, dV (key-tile outer)
+//
+// A work-group owns 128 keys (32 per wave).  K rows stay in registers as the B
+// operand of S = Q K^T; the V tile sits in LDS for the whole kernel and feeds
+// dP = dO V^T row-wise.  Query rows stream in stages of 32 (Q, dO, LSE, D),
+// double-buffered.  Two work-groups share a CU (256 registers per lane), so one
+// work-group's exp / dS arithmetic overlaps the other's matrix products.
 template <int D, bool CAUSAL, bool VARLEN>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fa_bwd_dkdv_kernel(AttnParams p) {
     using C = BwdKVCfg<D>;
     __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
+    const int wave_s = __builtin_amdgcn_readfirstlane(wave);
     const int h2 = lane >> 5;
     const int col = lane & 31;
     const int sl = lane & 15;
@@ -120,17 +124,22 @@ void fa_bwd_dkdv_kernel(AttnParams p) {
     const int kv_start = tile * C::BN;
     if (kv_start >= nk) return;
     const int64_t tok = (int64_t)p.H * D;
+    const int row_bytes = p.H * D * 2;
     const int kw0 = kv_start + wave * 32;   // this wave's first key
     const int key = kw0 + col;              // this lane's key (accumulator column)
+    FA_LDS char* lds = (FA_LDS char*)smem;
 
-    bf16x8 kf[C::KSTEPS], vf[C::KSTEPS];
+    // V tile -> LDS (rows past the sequence read as zeros)
+    {
+        const TileLoader<D, C::BN, C::NW> vload(row_bytes, wave, lane);
+        vload.load(lds, p.v + (int64_t)ks * tok + h * D, (uint32_t)nk * row_bytes,
+                   kv_start * row_bytes, wave_s);
+    }
+    bf16x8 kf[C::KSTEPS];
     {
         const int64_t off = (int64_t)(ks + min(key, nk - 1)) * tok + h * D + 8 * h2;
 #pragma unroll
-        for (int s = 0; s < C::KSTEPS; ++s) {
-            kf[s] = load16(p.k + off + 16 * s);
-            vf[s] = load16(p.v + off + 16 * s);
-        }
+        for (int s = 0; s < C::KSTEPS; ++s) kf[s] = load16(p.k + off + 16 * s);
     }
     f32x16 dka[C::DBLK], dva[C::DBLK];
 #pragma unroll
@@ -144,101 +153,97 @@ void fa_bwd_dkdv_kernel(AttnParams p) {
     const float c = p.scale_log2;
     const bf16* qbase = p.q + (int64_t)qs * tok + h * D;
     const bf16* gbase = p.dout + (int64_t)qs * tok + h * D;
+    const uint32_t q_bytes = (uint32_t)nq * row_bytes;
     const float* lbase = p.lse_in + ((int64_t)b * p.H + h) * p.nq;
     const float* dbase = p.dvec + ((int64_t)b * p.H + h) * p.nq;
-    const int q_first = CAUSAL ? (kv_start / C::BMQ) * C::BMQ : 0;
+    const uint32_t stat_bytes = (uint32_t)nq * 4;
+    const int q_first = CAUSAL ? kv_start : 0;   // BN is a multiple of BMQ
     const int n_q = nq > q_first ? (nq - q_first + C::BMQ - 1) / C::BMQ : 0;
+    const TileLoader<D, C::BMQ, C::NW> qload(row_bytes, wave, lane);
 
     auto issue = [&](int it) {
-        char* st = smem + (it & 1) * C::STAGE_BYTES;
+        FA_LDS char* st = lds + C::STAGE0 + (it & 1) * 2 * C::TILE_BYTES;
         const int q0 = q_first + it * C::BMQ;
-        load_tile_lds<D, C::BMQ, C::NW>(st, qbase, tok, q0, nq, wave, lane);
-        load_tile_lds<D, C::BMQ, C::NW>(st + C::TILE_BYTES, gbase, tok, q0, nq, wave, lane);
-        if (wave == 0) load_row_stats(st + 2 * C::TILE_BYTES, lbase, q0, nq, lane);
-        if (wave == 1) load_row_stats(st + 2 * C::TILE_BYTES + C::BMQ * 4, dbase, q0, nq, lane);
+        qload.load(st, qbase, q_bytes, q0 * row_bytes, wave_s);
+        qload.load(st + C::TILE_BYTES, gbase, q_bytes, q0 * row_bytes, wave_s);
+        FA_LDS char* sd = lds + C::STATS0 + (it & 1) * C::STAT_BYTES;
+        if (wave_s == 0) load_f32x64_lds(sd, lbase, stat_bytes, q0 * 4);
+        if (wave_s == 1) load_f32x64_lds(sd + 256, dbase, stat_bytes, q0 * 4);
     };
 
     if (n_q > 0) issue(0);
     for (int it = 0; it < n_q; ++it) {
-        char* st = smem + (it & 1) * C::STAGE_BYTES;
-        const char* qt = st;
-        const char* gt = st + C::TILE_BYTES;
-        const float* lse_t = reinterpret_cast<const float*>(st + 2 * C::TILE_BYTES);
-        const float* d_t = lse_t + C::BMQ;
+        const FA_LDS char* qt = lds + C::STAGE0 + (it & 1) * 2 * C::TILE_BYTES;
+        const FA_LDS char* gt = qt + C::TILE_BYTES;
+        const FA_LDS float* lse_t = (const FA_LDS float*)(lds + C::STATS0 + (it & 1) * C::STAT_BYTES);
+        const FA_LDS float* d_t = lse_t + 64;
         wait_vmem();
         __syncthreads();
         if (it + 1 < n_q) issue(it + 1);
         const int q0 = q_first + it * C::BMQ;
+        if (CAUSAL && q0 + 31 < kw0) continue;   // every query here precedes every key
 
+        // S = Q K^T and dP = dO V^T: rows are queries, columns this wave's keys
+        f32x16 s, dp;
 #pragma unroll
-        for (int qb = 0; qb < C::BMQ / 32; ++qb) {
-            const int qb0 = q0 + qb * 32;
-            if (CAUSAL && qb0 + 31 < kw0) continue;   // every query here precedes every key
+        for (int r = 0; r < 16; ++r) {
+            s[r] = 0.f;
+            dp[r] = 0.f;
+        }
+#pragma unroll
+        for (int k2 = 0; k2 < C::KSTEPS; ++k2) {
+            const int off = tile_off<D>(col, 2 * k2 + h2);
+            const bf16x8 vb = lds_read16(lds + tile_off<D>(wave * 32 + col, 2 * k2 + h2));
+            s = mfma_32x32x16(lds_read16(qt + off), kf[k2], s);
+            dp = mfma_32x32x16(lds_read16(gt + off), vb, dp);
+        }
 
-            // S = Q K^T and dP = dO V^T: rows are queries, columns this wave's keys
-            f32x16 s, dp;
+        // P = exp(scale*S - LSE), dS = P * (dP - D); this lane's rows are
+        // queries q0 + 8*(r/4) + 4*h2 + r%4.
+        const bool need_mask = (CAUSAL && q0 < kw0 + 31) || (q0 + 31 >= nq);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                s[r] = 0.f;
-                dp[r] = 0.f;
-            }
-            const int row = qb * 32 + col;
+        for (int rg = 0; rg < 4; ++rg) {
+            const int lr = 8 * rg + 4 * h2;
+            const f32x4 l4 = *reinterpret_cast<const FA_LDS f32x4*>(lse_t + lr);
+            const f32x4 d4 = *reinterpret_cast<const FA_LDS f32x4*>(d_t + lr);
 #pragma unroll
-            for (int k2 = 0; k2 < C::KSTEPS; ++k2) {
-                const int off = tile_off<D>(row, 2 * k2 + h2);
-                s = mfma_32x32x16(lds_read16((const FA_LDS char*)(qt + off)), kf[k2], s);
-                dp = mfma_32x32x16(lds_read16((const FA_LDS char*)(gt + off)), vf[k2], dp);
-            }
-
-            // P = exp(scale*S - LSE), dS = P * (dP - D); this lane's rows are
-            // queries qb0 + 8*(r/4) + 4*h2 + r%4.
-            const bool need_mask = (CAUSAL && qb0 < kw0 + 31) || (qb0 + 31 >= nq);
-#pragma unroll
-            for (int rg = 0; rg < 4; ++rg) {
-                const int lr = qb * 32 + 8 * rg + 4 * h2;
-                const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse_t + lr);
-                const f32x4 d4 = *reinterpret_cast<const f32x4*>(d_t + lr);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int r = 4 * rg + e;
-                    float pr = fast_exp2(__builtin_fmaf(s[r], c, -l4[e] * kLog2e));
-                    if (need_mask) {
-                        const int qrow = qb0 + 8 * rg + 4 * h2 + e;
-                        if ((CAUSAL && key > qrow) || qrow >= nq) pr = 0.f;
-                    }
-                    s[r] = pr;
-                    dp[r] = pr * (dp[r] - d4[e]);
+            for (int e = 0; e < 4; ++e) {
+                const int r = 4 * rg + e;
+                float pr = fast_exp2(__builtin_fmaf(s[r], c, -l4[e] * kLog2e));
+                if (need_mask) {
+                    const int qrow = q0 + lr + e;
+                    if ((CAUSAL && key > qrow) || qrow >= nq) pr = 0.f;
                 }
+                s[r] = pr;
+                dp[r] = pr * (dp[r] - d4[e]);
             }
-            bf16x8 pb[2], db[2];
+        }
+        bf16x8 pb[2], db[2];
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                float tp[8], td[8];
+        for (int kk = 0; kk < 2; ++kk) {
+            float tp[8], td[8];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    tp[e] = s[8 * kk + e];
-                    td[e] = dp[8 * kk + e];
-                }
-                pb[kk] = pack8(tp);
-                db[kk] = pack8(td);
+            for (int e = 0; e < 8; ++e) {
+                tp[e] = s[8 * kk + e];
+                td[e] = dp[8 * kk + e];
             }
+            pb[kk] = pack8(tp);
+            db[kk] = pack8(td);
+        }
 
-            // dV^T[dim][key] += dO^T P,  dK^T[dim][key] += Q^T dS
+        // dV^T[dim][key] += dO^T P,  dK^T[dim][key] += Q^T dS
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                const int r1 = qb * 32 + 16 * kk + 4 * h2;
+        for (int kk = 0; kk < 2; ++kk) {
+            const int r1 = 16 * kk + 4 * h2;
 #pragma unroll
-                for (int cb = 0; cb < C::DBLK; ++cb) {
-                    const int c0 = cb * 32 + 16 * g;
-                    const int o1 = tr_off<D>(r1, c0, sl);
-                    const int o2 = tr_off<D>(r1 + 8, c0, sl);
-                    const bf16x8 ag = join(lds_read_tr((const FA_LDS char*)(gt + o1)),
-                                           lds_read_tr((const FA_LDS char*)(gt + o2)));
-                    dva[cb] = mfma_32x32x16(ag, pb[kk], dva[cb]);
-                    const bf16x8 aq = join(lds_read_tr((const FA_LDS char*)(qt + o1)),
-                                           lds_read_tr((const FA_LDS char*)(qt + o2)));
-                    dka[cb] = mfma_32x32x16(aq, db[kk], dka[cb]);
-                }
+            for (int cb = 0; cb < C::DBLK; ++cb) {
+                const int c0 = cb * 32 + 16 * g;
+                const int o1 = tr_off<D>(r1, c0, sl);
+                const int o2 = tr_off<D>(r1 + 8, c0, sl);
+                const bf16x8 ag = join(lds_read_tr(gt + o1), lds_read_tr(gt + o2));
+                dva[cb] = mfma_32x32x16(ag, pb[kk], dva[cb]);
+                const bf16x8 aq = join(lds_read_tr(qt + o1), lds_read_tr(qt + o2));
+                dka[cb] = mfma_32x32x16(aq, db[kk], dka[cb]);
             }
         }
     }
@@ -312,20 +317,24 @@ void fa_bwd_dq_kernel(AttnParams p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[cb][r] = 0.f;
 
+    const int row_bytes = p.H * D * 2;
+    const uint32_t kv_bytes = (uint32_t)nk * row_bytes;
+    const TileLoader<D, C::BN, C::NW> loader(row_bytes, wave, lane);
+    FA_LDS char* lds = (FA_LDS char*)smem;
+    const int wave_s = __builtin_amdgcn_readfirstlane(wave);
     if (n_kv > 0) {
-        load_tile_lds<D, C::BN, C::NW>(smem, kbase, tok, 0, nk, wave, lane);
-        load_tile_lds<D, C::BN, C::NW>(smem + C::TILE_BYTES, vbase, tok, 0, nk, wave, lane);
+        loader.load(lds, kbase, kv_bytes, 0, wave_s);
+        loader.load(lds + C::TILE_BYTES, vbase, kv_bytes, 0, wave_s);
     }
     for (int t = 0; t < n_kv; ++t) {
-        char* kt = smem + (t & 1) * 2 * C::TILE_BYTES;
-        char* vt = kt + C::TILE_BYTES;
+        const FA_LDS char* kt = lds + (t & 1) * 2 * C::TILE_BYTES;
+        const FA_LDS char* vt = kt + C::TILE_BYTES;
         wait_vmem();
         __syncthreads();
         if (t + 1 < n_kv) {
-            char* kn = smem + ((t + 1) & 1) * 2 * C::TILE_BYTES;
-            load_tile_lds<D, C::BN, C::NW>(kn, kbase, tok, (t + 1) * C::BN, nk, wave, lane);
-            load_tile_lds<D, C::BN, C::NW>(kn + C::TILE_BYTES, vbase, tok, (t + 1) * C::BN, nk, wave,
-                                           lane);
+            FA_LDS char* kn = lds + ((t + 1) & 1) * 2 * C::TILE_BYTES;
+            loader.load(kn, kbase, kv_bytes, (t + 1) * C::BN * row_bytes, wave_s);
+            loader.load(kn + C::TILE_BYTES, vbase, kv_bytes, (t + 1) * C::BN * row_bytes, wave_s);
         }
         const int kv0 = t * C::BN;
         if (CAUSAL && kv0 > qw0 + 31) continue;
@@ -343,8 +352,8 @@ void fa_bwd_dq_kernel(AttnParams p) {
 #pragma unroll
             for (int k2 = 0; k2 < C::KSTEPS; ++k2) {
                 const int off = tile_off<D>(row, 2 * k2 + h2);
-                sT[kb] = mfma_32x32x16(lds_read16((const FA_LDS char*)(kt + off)), qf[k2], sT[kb]);
-                dpT[kb] = mfma_32x32x16(lds_read16((const FA_LDS char*)(vt + off)), gf[k2], dpT[kb]);
+                sT[kb] = mfma_32x32x16(lds_read16(kt + off), qf[k2], sT[kb]);
+                dpT[kb] = mfma_32x32x16(lds_read16(vt + off), gf[k2], dpT[kb]);
             }
         }
         const bool need_mask = (CAUSAL && kv0 + C::BN - 1 > qw0) || (kv0 + C::BN > nk);
@@ -374,8 +383,8 @@ void fa_bwd_dq_kernel(AttnParams p) {
 #pragma unroll
             for (int cb = 0; cb < C::DBLK; ++cb) {
                 const int c0 = cb * 32 + 16 * g;
-                const bf16x8 a = join(lds_read_tr((const FA_LDS char*)(kt + tr_off<D>(r1, c0, sl))),
-                                      lds_read_tr((const FA_LDS char*)(kt + tr_off<D>(r1 + 8, c0, sl))));
+                const bf16x8 a = join(lds_read_tr(kt + tr_off<D>(r1, c0, sl)),
+                                      lds_read_tr(kt + tr_off<D>(r1 + 8, c0, sl)));
                 acc[cb] = mfma_32x32x16(a, dsk[k2], acc[cb]);
             }
         }

@@ -101,6 +101,18 @@ __device__ __forceinline__ bf16x8 join(bf16x4 lo, bf16x4 hi) {
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+// 4 * (lane index), recomputed where it is used (volatile: never hoisted into a
+// register that would stay live across a loop).
+__device__ __forceinline__ int lane_x4_here() {
+    int v;
+    asm volatile(
+        "v_mbcnt_lo_u32_b32 %0, -1, 0\n\t"
+        "v_mbcnt_hi_u32_b32 %0, -1, %0\n\t"
+        "v_lshlrev_b32 %0, 2, %0"
+        : "=v"(v));
+    return v;
+}
+
 // Work-item order over a 1-D grid of `total` work-groups.  Consecutive
 // work-group ids are spread round-robin over the 8 XCDs (each with its own L2);
 // this maps XCD x to the contiguous logical range [x*total/8, (x+1)*total/8), so

@@ -102,4 +102,17 @@ struct TileLoader {
     }
 };
 
+// 64 consecutive fp32 values base[first..first+63] into LDS (one per lane, in
+// lane order), through a buffer resource whose range ends at `bytes`: values
+// past it read as zeros.  `first_bytes` = 4 * first (wave-uniform).
+__device__ __forceinline__ void load_f32x64_lds(FA_LDS char* lds, const float* base, uint32_t bytes,
+                                                int first_bytes) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    const auto rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), (short)0,
+                                                        (int)bytes, 0x00020000);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (FA_LDS void*)lds, 4, lane_x4_here(), first_bytes,
+                                             0, 0);
+#endif
+}
+
 }  // namespace fa355
