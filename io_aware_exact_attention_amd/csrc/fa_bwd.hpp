@@ -107,8 +107,7 @@ void fa_bwd_dkdv_kernel(AttnParams p) {
     __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
 
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: scalar branches
     const int h2 = lane >> 5;
     const int col = lane & 31;
     const int sl = lane & 15;
@@ -133,7 +132,7 @@ void fa_bwd_dkdv_kernel(AttnParams p) {
     {
         const TileLoader<D, C::BN, C::NW> vload(row_bytes, wave, lane);
         vload.load(lds, p.v + (int64_t)ks * tok + h * D, (uint32_t)nk * row_bytes,
-                   kv_start * row_bytes, wave_s);
+                   kv_start * row_bytes, wave);
     }
     bf16x8 kf[C::KSTEPS];
     {
@@ -164,11 +163,11 @@ void fa_bwd_dkdv_kernel(AttnParams p) {
     auto issue = [&](int it) {
         FA_LDS char* st = lds + C::STAGE0 + (it & 1) * 2 * C::TILE_BYTES;
         const int q0 = q_first + it * C::BMQ;
-        qload.load(st, qbase, q_bytes, q0 * row_bytes, wave_s);
-        qload.load(st + C::TILE_BYTES, gbase, q_bytes, q0 * row_bytes, wave_s);
+        qload.load(st, qbase, q_bytes, q0 * row_bytes, wave);
+        qload.load(st + C::TILE_BYTES, gbase, q_bytes, q0 * row_bytes, wave);
         FA_LDS char* sd = lds + C::STATS0 + (it & 1) * C::STAT_BYTES;
-        if (wave_s == 0) load_f32x64_lds(sd, lbase, stat_bytes, q0 * 4);
-        if (wave_s == 1) load_f32x64_lds(sd + 256, dbase, stat_bytes, q0 * 4);
+        if (wave == 0) load_f32x64_lds(sd, lbase, stat_bytes, q0 * 4);
+        if (wave == 1) load_f32x64_lds(sd + 256, dbase, stat_bytes, q0 * 4);
     };
 
     if (n_q > 0) issue(0);
@@ -198,9 +197,16 @@ void fa_bwd_dkdv_kernel(AttnParams p) {
             dp = mfma_32x32x16(lds_read16(gt + off), vb, dp);
         }
 
-        // P = exp(scale*S - LSE), dS = P * (dP - D); this lane's rows are
-        // queries q0 + 8*(r/4) + 4*h2 + r%4.
-        const bool need_mask = (CAUSAL && q0 < kw0 + 31) || (q0 + 31 >= nq);
+        // this lane's rows are queries q0 + 8*(r/4) + 4*h2 + r%4; masked scores
+        // become -inf so that their P is exactly 0
+        if ((CAUSAL && q0 < kw0 + 31) || (q0 + 31 >= nq)) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int qrow = q0 + 8 * (r >> 2) + 4 * h2 + (r & 3);
+                if ((CAUSAL && key > qrow) || qrow >= nq) s[r] = kNegInf;
+            }
+        }
+        // P = exp(scale*S - LSE), dS = P * (dP - D)
 #pragma unroll
         for (int rg = 0; rg < 4; ++rg) {
             const int lr = 8 * rg + 4 * h2;
@@ -209,11 +215,7 @@ void fa_bwd_dkdv_kernel(AttnParams p) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int r = 4 * rg + e;
-                float pr = fast_exp2(__builtin_fmaf(s[r], c, -l4[e] * kLog2e));
-                if (need_mask) {
-                    const int qrow = q0 + lr + e;
-                    if ((CAUSAL && key > qrow) || qrow >= nq) pr = 0.f;
-                }
+                const float pr = fast_exp2(__builtin_fmaf(s[r], c, -l4[e] * kLog2e));
                 s[r] = pr;
                 dp[r] = pr * (dp[r] - d4[e]);
             }
@@ -356,16 +358,21 @@ void fa_bwd_dq_kernel(AttnParams p) {
                 dpT[kb] = mfma_32x32x16(lds_read16(vt + off), gf[k2], dpT[kb]);
             }
         }
-        const bool need_mask = (CAUSAL && kv0 + C::BN - 1 > qw0) || (kv0 + C::BN > nk);
+        // masked scores become -inf so that their P is exactly 0
+        if ((CAUSAL && kv0 + C::BN - 1 > qw0) || (kv0 + C::BN > nk)) {
+#pragma unroll
+            for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int kj = kv0 + kb * 32 + 8 * (r >> 2) + 4 * h2 + (r & 3);
+                    if ((CAUSAL && kj > qi) || kj >= nk) sT[kb][r] = kNegInf;
+                }
+        }
 #pragma unroll
         for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                float pr = fast_exp2(__builtin_fmaf(sT[kb][r], c, -lse2));
-                if (need_mask) {
-                    const int kj = kv0 + kb * 32 + 8 * (r >> 2) + 4 * h2 + (r & 3);
-                    if ((CAUSAL && kj > qi) || kj >= nk) pr = 0.f;
-                }
+                const float pr = fast_exp2(__builtin_fmaf(sT[kb][r], c, -lse2));
                 sT[kb][r] = pr * (dpT[kb][r] - dd);   // dS^T
             }
         bf16x8 dsk[C::BN / 16];
