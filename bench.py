@@ -15,6 +15,7 @@ time-bounded sample of the same workload's heads.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -32,6 +33,49 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 CALIB_BYTES = 256 << 20     # size of the counter-calibration copy
 
 METRIC = "attention fwd & fwd+bwd TFLOP/s, % bf16 MFMA peak, B8 H16 N4096 d128 causal"
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(ROOT, "io_aware_exact_attention_amd", "csrc")
+
+
+def kernel_source_hash() -> str:
+    """sha256 over the HIP sources (sorted by name): identifies the kernels a
+    stored counter summary was taken from."""
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        if name.endswith((".hip", ".hpp")):
+            h.update(name.encode())
+            with open(os.path.join(CSRC, name), "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch of each kernel, from the committed rocprofv3 PMC summary
+    (TCC FETCH_SIZE and WRITE_SIZE in KiB, each scaled by what the same counter
+    read for the benchmark's calibration copy of known size).  None when there is
+    no summary or the kernels changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    src, calib, kern = None, None, {}
+    with open(path) as f:
+        for line in f:
+            t = line.split()
+            if not t or t[0].startswith("#"):
+                continue
+            if t[0] == "source_sha256":
+                src = t[1]
+            elif t[0] == "calibration_copy":
+                calib = (int(t[2]), float(t[4]), float(t[6]))   # bytes, fetch KiB, write KiB
+            elif t[0] == "kernel":
+                kern[t[1]] = (float(t[3]), float(t[5]))
+    if src != kernel_source_hash() or calib is None or calib[1] <= 0 or calib[2] <= 0:
+        return None
+    fetch_scale = calib[0] / (calib[1] * 1024)
+    write_scale = calib[0] / (calib[2] * 1024)
+    return {k: int(round(fk * 1024 * fetch_scale + wk * 1024 * write_scale))
+            for k, (fk, wk) in kern.items()}
 
 
 def parse():
@@ -149,17 +193,26 @@ def main():
         else:
             e["gbs"] = round(dot_bytes / (ms * 1e-3) / 1e9, 1)
         kern[n] = e
+    # algorithmic HBM bytes per launch (each input read once, each output written once)
+    tok = B * N * H
+    kern_bytes = [cnt["bytes_fwd"], dot_bytes, tok * (2 * 4 * d + 8) + tok * 2 * 2 * d,
+                  tok * (2 * 4 * d + 8) + tok * 2 * d]
+    traffic = measured_traffic(w.name)
     dom = max(range(len(names)), key=lambda i: kern_ms[i])
     if kern_flops[dom]:
         achieved = kern_flops[dom] / (kern_ms[dom] * 1e-3) / 1e12
         roof = {"kernel": names[dom], "bound": "mfma", "achieved": round(achieved, 2),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None}
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4)}
     else:
         achieved = dot_bytes / (kern_ms[dom] * 1e-3) / 1e9
         roof = {"kernel": names[dom], "bound": "hbm", "achieved": round(achieved, 1),
-                "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                "traffic": None}
+                "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4)}
+    roof["traffic"] = traffic.get(names[dom]) if traffic else None
+    roof["algorithmic_bytes"] = kern_bytes[dom]
+    for n, b_alg in zip(names, kern_bytes):
+        kern[n]["algorithmic_bytes"] = b_alg
+        kern[n]["traffic"] = traffic.get(n) if traffic else None
 
     t_fwd = kern_ms[0]
     t_bwd = sum(kern_ms[1:])
