@@ -142,15 +142,15 @@ def main():
     o = torch.empty_like(q)
     lse = torch.empty(B, H, N, dtype=torch.float32, device=dev)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    dvec = torch.empty(B, H, N, dtype=torch.float32, device=dev)
+    ws = torch.empty(fa355.fa_bwd_workspace_bytes(B, H, N, d) // 4, dtype=torch.float32, device=dev)
     scale = w.scale
 
     names = ["fa_fwd_kernel", "fa_bwd_dot_kernel", "fa_bwd_dkdv_kernel", "fa_bwd_dq_kernel"]
     calls = [
         lambda: fa355.fa_fwd(q, k, v, o, lse, scale, causal),
-        lambda: fa355.fa_bwd_dot(o, do, dvec),
-        lambda: fa355.fa_bwd_dkdv(q, k, v, do, lse, dvec, dk, dv, scale, causal),
-        lambda: fa355.fa_bwd_dq(q, k, v, do, lse, dvec, dq, scale, causal),
+        lambda: fa355.fa_bwd_dot(o, do, lse, ws),
+        lambda: fa355.fa_bwd_dkdv(q, k, v, do, ws, dk, dv, scale, causal),
+        lambda: fa355.fa_bwd_dq(q, k, v, do, ws, dq, scale, causal),
     ]
     # One plain device copy of known size, outside the timed region: under
     # rocprofv3 --pmc its FETCH_SIZE / WRITE_SIZE calibrate the byte counters.
@@ -184,7 +184,7 @@ def main():
     f_fwd, f_bwd = cnt["flops_fwd"], cnt["flops_bwd"]
     # algorithmic FLOPs / bytes attributed per kernel (the 10d backward = 8d in dK/dV + 2d in dQ)
     kern_flops = [f_fwd, 0, 8 * d * pairs, 2 * d * pairs]
-    dot_bytes = B * N * H * (2 * 2 * d + 4)
+    dot_bytes = B * N * H * (2 * 2 * d + 4 + 8)   # O, dO, LSE in; -D, LSE*log2(e) out
     kern = {}
     for n, ms, fl in zip(names, kern_ms, kern_flops):
         e = {"ms": round(ms, 4)}

@@ -91,8 +91,9 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* l
                   int causal, void* stream);
 
 /*
- * Bytes of device workspace fa_bwd / fa_bwd_varlen need: one fp32 value per
- * query row and head (D_i = sum_c dO_ic * O_ic), laid out like lse.
+ * Bytes of device workspace fa_bwd / fa_bwd_varlen need: two fp32 planes, each
+ * with one value per query row and head laid out like lse: -D_i, where
+ * D_i = sum_c dO_ic * O_ic, then LSE_i * log2(e).
  * batch_or_nseq = B (dense) or nseq (varlen); nq = Nq (dense) or max_seqlen_q.
  * Returns 0 for non-positive arguments.
  */
@@ -113,20 +114,23 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
 /*
  * The three stages fa_bwd runs, exposed separately (dense batch only) for callers
  * that time them or need only some gradients.  Arguments mean what they mean in
- * fa_bwd; `dvec` is the fp32 row vector D [B,H,Nq] (fa_bwd's workspace).
- *   fa_bwd_dot:  D_i = sum_c dO_ic * O_ic                    (writes dvec)
- *   fa_bwd_dkdv: dK, dV from q, k, v, dout, lse, dvec         (writes dk, dv)
- *   fa_bwd_dq:   dQ from q, k, v, dout, lse, dvec             (writes dq)
- * fa_bwd_dkdv and fa_bwd_dq both need dvec from fa_bwd_dot on the same stream.
+ * fa_bwd; `workspace` is fa_bwd's workspace (fa_bwd_workspace_bytes(B,H,Nq,d)
+ * bytes, 4-byte aligned).
+ *   fa_bwd_dot:  fills the workspace: -D_i (D_i = sum_c dO_ic * O_ic) and
+ *                LSE_i * log2(e), from o, dout and lse
+ *   fa_bwd_dkdv: dK, dV from q, k, v, dout and the workspace   (writes dk, dv)
+ *   fa_bwd_dq:   dQ from q, k, v, dout and the workspace       (writes dq)
+ * fa_bwd_dkdv and fa_bwd_dq both need the workspace that fa_bwd_dot filled on the
+ * same stream.  Errors as fa_bwd.
  */
-int fa_bwd_dot(const void* o, const void* dout, float* dvec, int B, int H, int Nq, int d,
-               void* stream);
-int fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, const float* lse,
-                const float* dvec, void* dk, void* dv, int B, int H, int Nq, int Nk, int d,
-                float scale, int causal, void* stream);
-int fa_bwd_dq(const void* q, const void* k, const void* v, const void* dout, const float* lse,
-              const float* dvec, void* dq, int B, int H, int Nq, int Nk, int d, float scale,
-              int causal, void* stream);
+int fa_bwd_dot(const void* o, const void* dout, const float* lse, void* workspace,
+               size_t workspace_bytes, int B, int H, int Nq, int d, void* stream);
+int fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout,
+                const void* workspace, size_t workspace_bytes, void* dk, void* dv, int B, int H,
+                int Nq, int Nk, int d, float scale, int causal, void* stream);
+int fa_bwd_dq(const void* q, const void* k, const void* v, const void* dout,
+              const void* workspace, size_t workspace_bytes, void* dq, int B, int H, int Nq,
+              int Nk, int d, float scale, int causal, void* stream);
 
 /* Backward, packed variable-length batch; arguments as fa_fwd_varlen and fa_bwd. */
 int fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o,

@@ -136,6 +136,12 @@ int launch_bwd(const AttnParams& p, int d, int causal, hipStream_t s, int stages
     return st;
 }
 
+// The backward workspace holds two fp32 planes laid out like lse: -D, then LSE * log2(e).
+void set_workspace(AttnParams& p, void* ws) {
+    p.dvec = static_cast<float*>(ws);
+    p.lse2 = p.dvec + (size_t)p.batch * p.H * p.nq;
+}
+
 AttnParams base_params(const void* q, const void* k, const void* v, int batch, int H, int nq,
                        int nk, float scale) {
     AttnParams p;
@@ -223,7 +229,7 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* l
 size_t fa_bwd_workspace_bytes(int batch_or_nseq, int H, int nq, int d) {
     (void)d;
     if (batch_or_nseq <= 0 || H <= 0 || nq <= 0) return 0;
-    return sizeof(float) * (size_t)batch_or_nseq * (size_t)H * (size_t)nq;
+    return 2 * sizeof(float) * (size_t)batch_or_nseq * (size_t)H * (size_t)nq;
 }
 
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
@@ -248,64 +254,67 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
     p.dq = static_cast<bf16*>(dq);
     p.dk = static_cast<bf16*>(dk);
     p.dv = static_cast<bf16*>(dv);
-    p.dvec = static_cast<float*>(workspace);
+    set_workspace(p, workspace);
     return launch_bwd<false>(p, d, causal, static_cast<hipStream_t>(stream));
 }
 
-int fa_bwd_dot(const void* o, const void* dout, float* dvec, int B, int H, int Nq, int d,
-               void* stream) {
-    if (!o || !dout || !dvec) return FA_ERR_NULL;
+int fa_bwd_dot(const void* o, const void* dout, const float* lse, void* workspace,
+               size_t workspace_bytes, int B, int H, int Nq, int d, void* stream) {
+    if (!o || !dout || !lse) return FA_ERR_NULL;
     if (B <= 0 || Nq <= 0) return FA_ERR_SHAPE;
     int st = check_common(H, d, 1.f, 0);
     if (st) return st;
-    if (!aligned(o, 16) || !aligned(dout, 16) || !aligned(dvec, 4)) return FA_ERR_ALIGN;
+    if (!workspace || workspace_bytes < fa_bwd_workspace_bytes(B, H, Nq, d)) return FA_ERR_WORKSPACE;
+    if (!aligned(o, 16) || !aligned(dout, 16) || !aligned(lse, 4) || !aligned(workspace, 4))
+        return FA_ERR_ALIGN;
     st = check_sizes((int64_t)B * Nq, (int64_t)B * Nq, Nq, Nq, H, d, (int64_t)((Nq + 15) / 16) * H * B);
     if (st) return st;
     AttnParams p = base_params(nullptr, nullptr, nullptr, B, H, Nq, Nq, 1.f);
     p.o_in = static_cast<const bf16*>(o);
     p.dout = static_cast<const bf16*>(dout);
-    p.dvec = dvec;
+    p.lse_in = lse;
+    set_workspace(p, workspace);
     return launch_bwd<false>(p, d, 0, static_cast<hipStream_t>(stream), kStageDot);
 }
 
 static int bwd_stage(int stage, const void* q, const void* k, const void* v, const void* dout,
-                     const float* lse, const float* dvec, void* dq, void* dk, void* dv, int B, int H,
-                     int Nq, int Nk, int d, float scale, int causal, void* stream) {
-    if (!q || !k || !v || !dout || !lse || !dvec) return FA_ERR_NULL;
+                     const void* workspace, size_t workspace_bytes, void* dq, void* dk, void* dv,
+                     int B, int H, int Nq, int Nk, int d, float scale, int causal, void* stream) {
+    if (!q || !k || !v || !dout) return FA_ERR_NULL;
     if (stage == kStageDkdv && (!dk || !dv)) return FA_ERR_NULL;
     if (stage == kStageDq && !dq) return FA_ERR_NULL;
     if (B <= 0 || Nq <= 0 || Nk <= 0) return FA_ERR_SHAPE;
     int st = check_common(H, d, scale, causal);
     if (st) return st;
     if (causal && Nq != Nk) return FA_ERR_UNSUPPORTED;
+    if (!workspace || workspace_bytes < fa_bwd_workspace_bytes(B, H, Nq, d)) return FA_ERR_WORKSPACE;
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(dout, 16) ||
-        !aligned(lse, 4) || !aligned(dvec, 4) || (dq && !aligned(dq, 16)) ||
-        (dk && !aligned(dk, 16)) || (dv && !aligned(dv, 16)))
+        !aligned(workspace, 4) || (dq && !aligned(dq, 16)) || (dk && !aligned(dk, 16)) ||
+        (dv && !aligned(dv, 16)))
         return FA_ERR_ALIGN;
     st = check_sizes((int64_t)B * Nq, (int64_t)B * Nk, Nq, Nk, H, d, (int64_t)((Nq + 15) / 16) * H * B);
     if (st) return st;
     AttnParams p = base_params(q, k, v, B, H, Nq, Nk, scale);
     p.dout = static_cast<const bf16*>(dout);
-    p.lse_in = lse;
-    p.dvec = const_cast<float*>(dvec);
+    set_workspace(p, const_cast<void*>(workspace));
     p.dq = static_cast<bf16*>(dq);
     p.dk = static_cast<bf16*>(dk);
     p.dv = static_cast<bf16*>(dv);
     return launch_bwd<false>(p, d, causal, static_cast<hipStream_t>(stream), stage);
 }
 
-int fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, const float* lse,
-                const float* dvec, void* dk, void* dv, int B, int H, int Nq, int Nk, int d,
+int fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, const void* workspace,
+                size_t workspace_bytes, void* dk, void* dv, int B, int H, int Nq, int Nk, int d,
                 float scale, int causal, void* stream) {
-    return bwd_stage(kStageDkdv, q, k, v, dout, lse, dvec, nullptr, dk, dv, B, H, Nq, Nk, d, scale,
-                     causal, stream);
+    return bwd_stage(kStageDkdv, q, k, v, dout, workspace, workspace_bytes, nullptr, dk, dv, B, H, Nq,
+                     Nk, d, scale, causal, stream);
 }
 
-int fa_bwd_dq(const void* q, const void* k, const void* v, const void* dout, const float* lse,
-              const float* dvec, void* dq, int B, int H, int Nq, int Nk, int d, float scale,
+int fa_bwd_dq(const void* q, const void* k, const void* v, const void* dout, const void* workspace,
+              size_t workspace_bytes, void* dq, int B, int H, int Nq, int Nk, int d, float scale,
               int causal, void* stream) {
-    return bwd_stage(kStageDq, q, k, v, dout, lse, dvec, dq, nullptr, nullptr, B, H, Nq, Nk, d, scale,
-                     causal, stream);
+    return bwd_stage(kStageDq, q, k, v, dout, workspace, workspace_bytes, dq, nullptr, nullptr, B, H,
+                     Nq, Nk, d, scale, causal, stream);
 }
 
 int fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o, const void* dout,
@@ -341,7 +350,7 @@ int fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o, co
     p.dq = static_cast<bf16*>(dq);
     p.dk = static_cast<bf16*>(dk);
     p.dv = static_cast<bf16*>(dv);
-    p.dvec = static_cast<float*>(workspace);
+    set_workspace(p, workspace);
     p.cu_q = cu_seqlens_q;
     p.cu_k = cu_seqlens_k;
     return launch_bwd<true>(p, d, causal, s);

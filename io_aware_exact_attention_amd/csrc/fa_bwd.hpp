@@ -9,7 +9,9 @@
 //
 // Three kernels, all stream-ordered and free of atomics (every output element
 // is owned by exactly one work-group, so results are bitwise deterministic):
-//   1. fa_bwd_dot_kernel:  D_i = rowsum(dO * O), one pass over O and dO.
+//   1. fa_bwd_dot_kernel:  D_i = rowsum(dO * O), one pass over O and dO; it
+//      stores -D_i and LSE_i * log2(e), the forms the other two kernels consume
+//      (-D seeds the dP accumulator, so dP - D costs no arithmetic).
 //   2. fa_bwd_dkdv_kernel: key-tile outer.  A work-group owns a 128-key tile
 //      (K rows in registers, 32 keys per wave; V in LDS) and keeps the dK^T,
 //      dV^T accumulators on chip, streams the query rows that can see those keys
@@ -33,7 +35,9 @@ template <int D>
 struct BwdPreCfg {
     static constexpr int THREADS = 256;
     static constexpr int TPR = D / 8;             // threads per (row, head): 16 bytes each
-    static constexpr int ROWS = THREADS / TPR;
+    static constexpr int GROUPS = THREADS / TPR;  // rows in flight per pass
+    static constexpr int RPT = 4;                 // passes: rows per thread group
+    static constexpr int ROWS = GROUPS * RPT;     // rows per work-group
 };
 
 template <int D>
@@ -44,7 +48,7 @@ struct BwdKVCfg {
     static constexpr int ROW_BYTES = D * 2;
     static constexpr int TILE_BYTES = BMQ * ROW_BYTES;
     static constexpr int V_BYTES = BN * ROW_BYTES;
-    static constexpr int STAT_BYTES = 512;        // 64 LSE then 64 D values, fp32
+    static constexpr int STAT_BYTES = 512;        // 64 LSE*log2(e) then 64 -D values, fp32
     // [V tile][Q | dO stage 0][Q | dO stage 1][stats 0][stats 1]
     static constexpr int STAGE0 = V_BYTES;
     static constexpr int STATS0 = V_BYTES + 4 * TILE_BYTES;
@@ -67,7 +71,7 @@ struct BwdQCfg {
 };
 
 // ---------------------------------------------------------------------------
-// 1. D_i = sum_c dO_ic * O_ic  (fp32, laid out like LSE)
+// 1. D_i = sum_c dO_ic * O_ic; writes -D_i and LSE_i * log2(e) (fp32, laid out like LSE)
 template <int D, bool VARLEN>
 __global__ __launch_bounds__(256) void fa_bwd_dot_kernel(AttnParams p) {
     using C = BwdPreCfg<D>;
@@ -77,19 +81,34 @@ __global__ __launch_bounds__(256) void fa_bwd_dot_kernel(AttnParams p) {
     const int b = bh / p.H;
     int qs, nq, ks, nk;
     seq_range<VARLEN>(p, b, qs, nq, ks, nk);
-    const int r = tile * C::ROWS + (int)threadIdx.x / C::TPR;
+    const int grp = (int)threadIdx.x / C::TPR;
     const int c8 = (int)threadIdx.x % C::TPR;
-    float acc = 0.f;
-    if (r < nq) {
-        const int64_t off = (int64_t)(qs + r) * p.H * D + h * D + 8 * c8;
-        const bf16x8 o = load16(p.o_in + off);
-        const bf16x8 g = load16(p.dout + off);
+    bf16x8 o[C::RPT], g[C::RPT];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc = __builtin_fmaf((float)o[e], (float)g[e], acc);
+    for (int j = 0; j < C::RPT; ++j) {   // all loads first: RPT rows in flight per thread
+        const int r = tile * C::ROWS + j * C::GROUPS + grp;
+        if (r < nq) {
+            const int64_t off = (int64_t)(qs + r) * p.H * D + h * D + 8 * c8;
+            o[j] = load16(p.o_in + off);
+            g[j] = load16(p.dout + off);
+        }
     }
 #pragma unroll
-    for (int w = C::TPR / 2; w > 0; w >>= 1) acc += __shfl_xor(acc, w);
-    if (c8 == 0 && r < nq) p.dvec[((int64_t)b * p.H + h) * p.nq + r] = acc;
+    for (int j = 0; j < C::RPT; ++j) {
+        const int r = tile * C::ROWS + j * C::GROUPS + grp;
+        float acc = 0.f;
+        if (r < nq) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc = __builtin_fmaf((float)o[j][e], (float)g[j][e], acc);
+        }
+#pragma unroll
+        for (int w = C::TPR / 2; w > 0; w >>= 1) acc += __shfl_xor(acc, w);
+        if (c8 == 0 && r < nq) {
+            const int64_t i = ((int64_t)b * p.H + h) * p.nq + r;
+            p.dvec[i] = -acc;
+            p.lse2[i] = p.lse_in[i] * kLog2e;
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -153,7 +172,7 @@ void fa_bwd_dkdv_kernel(AttnParams p) {
     const bf16* qbase = p.q + (int64_t)qs * tok + h * D;
     const bf16* gbase = p.dout + (int64_t)qs * tok + h * D;
     const uint32_t q_bytes = (uint32_t)nq * row_bytes;
-    const float* lbase = p.lse_in + ((int64_t)b * p.H + h) * p.nq;
+    const float* lbase = p.lse2 + ((int64_t)b * p.H + h) * p.nq;
     const float* dbase = p.dvec + ((int64_t)b * p.H + h) * p.nq;
     const uint32_t stat_bytes = (uint32_t)nq * 4;
     const int q_first = CAUSAL ? kv_start : 0;   // BN is a multiple of BMQ
@@ -175,19 +194,25 @@ void fa_bwd_dkdv_kernel(AttnParams p) {
         const FA_LDS char* qt = lds + C::STAGE0 + (it & 1) * 2 * C::TILE_BYTES;
         const FA_LDS char* gt = qt + C::TILE_BYTES;
         const FA_LDS float* lse_t = (const FA_LDS float*)(lds + C::STATS0 + (it & 1) * C::STAT_BYTES);
-        const FA_LDS float* d_t = lse_t + 64;
+        const FA_LDS float* nd_t = lse_t + 64;
         wait_vmem();
         __syncthreads();
         if (it + 1 < n_q) issue(it + 1);
         const int q0 = q_first + it * C::BMQ;
         if (CAUSAL && q0 + 31 < kw0) continue;   // every query here precedes every key
 
-        // S = Q K^T and dP = dO V^T: rows are queries, columns this wave's keys
+        // S = Q K^T and dP - D = dO V^T - D: rows are queries (this lane's rows are
+        // q0 + 8*(r/4) + 4*h2 + r%4), columns this wave's keys.  The dP
+        // accumulator starts at -D of its row.
         f32x16 s, dp;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            s[r] = 0.f;
-            dp[r] = 0.f;
+        for (int rg = 0; rg < 4; ++rg) {
+            const f32x4 n4 = *reinterpret_cast<const FA_LDS f32x4*>(nd_t + 8 * rg + 4 * h2);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                s[4 * rg + e] = 0.f;
+                dp[4 * rg + e] = n4[e];
+            }
         }
 #pragma unroll
         for (int k2 = 0; k2 < C::KSTEPS; ++k2) {
@@ -197,8 +222,7 @@ void fa_bwd_dkdv_kernel(AttnParams p) {
             dp = mfma_32x32x16(lds_read16(gt + off), vb, dp);
         }
 
-        // this lane's rows are queries q0 + 8*(r/4) + 4*h2 + r%4; masked scores
-        // become -inf so that their P is exactly 0
+        // masked scores become -inf so that their P is exactly 0
         if ((CAUSAL && q0 < kw0 + 31) || (q0 + 31 >= nq)) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
@@ -206,18 +230,16 @@ void fa_bwd_dkdv_kernel(AttnParams p) {
                 if ((CAUSAL && key > qrow) || qrow >= nq) s[r] = kNegInf;
             }
         }
-        // P = exp(scale*S - LSE), dS = P * (dP - D)
+        // P = exp(scale*S - LSE) = exp2(S * scale*log2(e) - LSE*log2(e)), dS = P * (dP - D)
 #pragma unroll
         for (int rg = 0; rg < 4; ++rg) {
-            const int lr = 8 * rg + 4 * h2;
-            const f32x4 l4 = *reinterpret_cast<const FA_LDS f32x4*>(lse_t + lr);
-            const f32x4 d4 = *reinterpret_cast<const FA_LDS f32x4*>(d_t + lr);
+            const f32x4 l4 = *reinterpret_cast<const FA_LDS f32x4*>(lse_t + 8 * rg + 4 * h2);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int r = 4 * rg + e;
-                const float pr = fast_exp2(__builtin_fmaf(s[r], c, -l4[e] * kLog2e));
+                const float pr = fast_exp2(__builtin_fmaf(s[r], c, -l4[e]));
                 s[r] = pr;
-                dp[r] = pr * (dp[r] - d4[e]);
+                dp[r] = pr * dp[r];
             }
         }
         bf16x8 pb[2], db[2];
@@ -236,12 +258,13 @@ void fa_bwd_dkdv_kernel(AttnParams p) {
         // dV^T[dim][key] += dO^T P,  dK^T[dim][key] += Q^T dS
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
-            const int r1 = 16 * kk + 4 * h2;
 #pragma unroll
             for (int cb = 0; cb < C::DBLK; ++cb) {
                 const int c0 = cb * 32 + 16 * g;
-                const int o1 = tr_off<D>(r1, c0, sl);
-                const int o2 = tr_off<D>(r1 + 8, c0, sl);
+                // rows 16*kk + 4*h2 (+8): 16 more rows keep the swizzle, so kk only
+                // adds an immediate offset
+                const int o1 = tr_off<D>(4 * h2, c0, sl) + kk * 16 * C::ROW_BYTES;
+                const int o2 = tr_off<D>(4 * h2 + 8, c0, sl) + kk * 16 * C::ROW_BYTES;
                 const bf16x8 ag = join(lds_read_tr(gt + o1), lds_read_tr(gt + o2));
                 dva[cb] = mfma_32x32x16(ag, pb[kk], dva[cb]);
                 const bf16x8 aq = join(lds_read_tr(qt + o1), lds_read_tr(qt + o2));
@@ -309,8 +332,8 @@ void fa_bwd_dq_kernel(AttnParams p) {
         }
     }
     const int64_t srow = ((int64_t)b * p.H + h) * p.nq + qrow;
-    const float lse2 = p.lse_in[srow] * kLog2e;
-    const float dd = p.dvec[srow];
+    const float lse2 = p.lse2[srow];   // LSE * log2(e)
+    const float nd = p.dvec[srow];     // -D
     const float c = p.scale_log2;
 
     f32x16 acc[C::DBLK];
@@ -373,7 +396,7 @@ void fa_bwd_dq_kernel(AttnParams p) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const float pr = fast_exp2(__builtin_fmaf(sT[kb][r], c, -lse2));
-                sT[kb][r] = pr * (dpT[kb][r] - dd);   // dS^T
+                sT[kb][r] = pr * (dpT[kb][r] + nd);   // dS^T
             }
         bf16x8 dsk[C::BN / 16];
 #pragma unroll
@@ -386,12 +409,12 @@ void fa_bwd_dq_kernel(AttnParams p) {
         // dQ^T[dim][query] += K^T dS^T, K^T via transposed LDS reads
 #pragma unroll
         for (int k2 = 0; k2 < C::BN / 16; ++k2) {
-            const int r1 = 16 * k2 + 4 * h2;
 #pragma unroll
             for (int cb = 0; cb < C::DBLK; ++cb) {
                 const int c0 = cb * 32 + 16 * g;
-                const bf16x8 a = join(lds_read_tr(kt + tr_off<D>(r1, c0, sl)),
-                                      lds_read_tr(kt + tr_off<D>(r1 + 8, c0, sl)));
+                const int rk = k2 * 16 * C::ROW_BYTES;   // 16 more rows keep the swizzle
+                const bf16x8 a = join(lds_read_tr(kt + tr_off<D>(4 * h2, c0, sl) + rk),
+                                      lds_read_tr(kt + tr_off<D>(4 * h2 + 8, c0, sl) + rk));
                 acc[cb] = mfma_32x32x16(a, dsk[k2], acc[cb]);
             }
         }

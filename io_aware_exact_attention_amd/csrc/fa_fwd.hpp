@@ -180,12 +180,12 @@ void fa_fwd_kernel(AttnParams p) {
         const int g = (lane >> 4) & 1;
 #pragma unroll
         for (int ks2 = 0; ks2 < C::BN / 16; ++ks2) {
-            const int r1 = 16 * ks2 + 4 * h2;
 #pragma unroll
             for (int cb = 0; cb < C::DBLK; ++cb) {
                 const int c0 = cb * 32 + 16 * g;
-                bf16x8 a = join(lds_read_tr((const FA_LDS char*)(vt + tr_off<D>(r1, c0, sl))),
-                                lds_read_tr((const FA_LDS char*)(vt + tr_off<D>(r1 + 8, c0, sl))));
+                const int rk = ks2 * 16 * C::ROW_BYTES;   // 16 more rows keep the swizzle
+                bf16x8 a = join(lds_read_tr((const FA_LDS char*)(vt + tr_off<D>(4 * h2, c0, sl) + rk)),
+                                lds_read_tr((const FA_LDS char*)(vt + tr_off<D>(4 * h2 + 8, c0, sl) + rk)));
                 acc[cb] = mfma_32x32x16(a, pk[ks2], acc[cb]);
             }
         }

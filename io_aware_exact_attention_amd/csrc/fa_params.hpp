@@ -17,7 +17,8 @@ struct AttnParams {
     bf16* dq;
     bf16* dk;
     bf16* dv;
-    float* dvec;         // backward workspace: D_i = rowsum(dO * O), laid out like lse
+    float* dvec;         // backward workspace plane 0: -D_i = -rowsum(dO * O), laid out like lse
+    float* lse2;         // backward workspace plane 1: LSE_i * log2(e), laid out like lse
     const int* cu_q;     // varlen prefix offsets (nseq+1), else null
     const int* cu_k;
     int batch;           // B, or nseq for varlen

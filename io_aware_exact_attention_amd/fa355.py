@@ -33,9 +33,9 @@ _SIGNATURES = {
     "fa_bwd_workspace_bytes": (_sz, [_c_int] * 4),
     "fa_bwd": (_c_int, [_vp] * 10 + [_sz] + [_c_int] * 5 + [_c_float, _c_int, _vp]),
     "fa_bwd_varlen": (_c_int, [_vp] * 10 + [_sz] + [_vp] * 2 + [_c_int] * 5 + [_c_float, _c_int, _vp]),
-    "fa_bwd_dot": (_c_int, [_vp] * 3 + [_c_int] * 4 + [_vp]),
-    "fa_bwd_dkdv": (_c_int, [_vp] * 8 + [_c_int] * 5 + [_c_float, _c_int, _vp]),
-    "fa_bwd_dq": (_c_int, [_vp] * 7 + [_c_int] * 5 + [_c_float, _c_int, _vp]),
+    "fa_bwd_dot": (_c_int, [_vp] * 4 + [_sz] + [_c_int] * 4 + [_vp]),
+    "fa_bwd_dkdv": (_c_int, [_vp] * 5 + [_sz] + [_vp] * 2 + [_c_int] * 5 + [_c_float, _c_int, _vp]),
+    "fa_bwd_dq": (_c_int, [_vp] * 5 + [_sz] + [_vp] + [_c_int] * 5 + [_c_float, _c_int, _vp]),
 }
 
 STATUS = {0: "FA_OK", -1: "FA_ERR_NULL", -2: "FA_ERR_SHAPE", -3: "FA_ERR_UNSUPPORTED",
@@ -116,21 +116,25 @@ def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, scale: float, causal: b
                         float(scale), int(bool(causal)), _stream(stream)))
 
 
-def fa_bwd_dot(o, dout, dvec, stream=None):
+def fa_bwd_dot(o, dout, lse, workspace, stream=None):
     B, Nq, H, d = o.shape
-    _check(lib().fa_bwd_dot(_ptr(o), _ptr(dout), _ptr(dvec), B, H, Nq, d, _stream(stream)))
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(lib().fa_bwd_dot(_ptr(o), _ptr(dout), _ptr(lse), _ptr(workspace), nbytes, B, H, Nq, d,
+                            _stream(stream)))
 
 
-def fa_bwd_dkdv(q, k, v, dout, lse, dvec, dk, dv, scale: float, causal: bool, stream=None):
+def fa_bwd_dkdv(q, k, v, dout, workspace, dk, dv, scale: float, causal: bool, stream=None):
     B, H, Nq, Nk, d = _dense_dims(q, k)
-    _check(lib().fa_bwd_dkdv(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(lse), _ptr(dvec),
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(lib().fa_bwd_dkdv(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(workspace), nbytes,
                              _ptr(dk), _ptr(dv), B, H, Nq, Nk, d, float(scale),
                              int(bool(causal)), _stream(stream)))
 
 
-def fa_bwd_dq(q, k, v, dout, lse, dvec, dq, scale: float, causal: bool, stream=None):
+def fa_bwd_dq(q, k, v, dout, workspace, dq, scale: float, causal: bool, stream=None):
     B, H, Nq, Nk, d = _dense_dims(q, k)
-    _check(lib().fa_bwd_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(lse), _ptr(dvec),
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(lib().fa_bwd_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(workspace), nbytes,
                            _ptr(dq), B, H, Nq, Nk, d, float(scale), int(bool(causal)),
                            _stream(stream)))
 

@@ -46,7 +46,7 @@ def test_status_strings_and_version():
 
 
 def test_workspace_bytes():
-    assert fa355.fa_bwd_workspace_bytes(8, 16, 4096, 128) == 4 * 8 * 16 * 4096
+    assert fa355.fa_bwd_workspace_bytes(8, 16, 4096, 128) == 2 * 4 * 8 * 16 * 4096
     assert fa355.fa_bwd_workspace_bytes(0, 16, 4096, 128) == 0
     assert fa355.fa_bwd_workspace_bytes(2, -1, 4, 64) == 0
 
@@ -73,7 +73,7 @@ def test_fwd_rejects(kw, code):
 def test_bwd_rejects():
     assert _bwd(ptrs=[A] * 8 + [None]) == -1
     assert _bwd(ws=None) == -6
-    assert _bwd(wsb=4 * 16 - 1) == -6
+    assert _bwd(wsb=2 * 4 * 16 - 1) == -6
     assert _bwd(d=80) == -3
     assert _bwd(causal=1, Nk=8) == -3
     assert _bwd(ptrs=[A] * 6 + [MIS] + [A] * 2) == -4
@@ -96,14 +96,19 @@ def test_varlen_rejects():
 
 def test_stage_entry_points_reject():
     lib = fa355.lib()
-    assert lib.fa_bwd_dot(None, A, A, 1, 1, 16, 64, None) == -1
-    assert lib.fa_bwd_dot(A, A, A, 1, 1, 16, 72, None) == -3
-    assert lib.fa_bwd_dot(A, MIS, A, 1, 1, 16, 64, None) == -4
-    assert lib.fa_bwd_dkdv(*[A] * 6, None, A, 1, 1, 16, 16, 64, 0.1, 0, None) == -1
-    assert lib.fa_bwd_dkdv(*[A] * 8, 1, 1, 16, 8, 64, 0.1, 1, None) == -3
-    assert lib.fa_bwd_dq(*[A] * 6, None, 1, 1, 16, 16, 64, 0.1, 0, None) == -1
-    assert lib.fa_bwd_dq(*[A] * 6, MIS, 1, 1, 16, 16, 64, 0.1, 0, None) == -4
-    assert lib.fa_bwd_dq(*[A] * 7, 1, 1, 0, 16, 64, 0.1, 0, None) == -2
+    W = 1 << 20
+    assert lib.fa_bwd_dot(None, A, A, A, W, 1, 1, 16, 64, None) == -1
+    assert lib.fa_bwd_dot(A, A, None, A, W, 1, 1, 16, 64, None) == -1
+    assert lib.fa_bwd_dot(A, A, A, A, W, 1, 1, 16, 72, None) == -3
+    assert lib.fa_bwd_dot(A, MIS, A, A, W, 1, 1, 16, 64, None) == -4
+    assert lib.fa_bwd_dot(A, A, A, None, W, 1, 1, 16, 64, None) == -6
+    assert lib.fa_bwd_dot(A, A, A, A, 2 * 4 * 16 - 1, 1, 1, 16, 64, None) == -6
+    assert lib.fa_bwd_dkdv(*[A] * 4, A, W, None, A, 1, 1, 16, 16, 64, 0.1, 0, None) == -1
+    assert lib.fa_bwd_dkdv(*[A] * 4, A, W, A, A, 1, 1, 16, 8, 64, 0.1, 1, None) == -3
+    assert lib.fa_bwd_dkdv(*[A] * 4, A, 8, A, A, 1, 1, 16, 16, 64, 0.1, 0, None) == -6
+    assert lib.fa_bwd_dq(*[A] * 4, A, W, None, 1, 1, 16, 16, 64, 0.1, 0, None) == -1
+    assert lib.fa_bwd_dq(*[A] * 4, A, W, MIS, 1, 1, 16, 16, 64, 0.1, 0, None) == -4
+    assert lib.fa_bwd_dq(*[A] * 4, A, W, A, 1, 1, 0, 16, 64, 0.1, 0, None) == -2
 
 
 def test_binding_raises_on_error():
