@@ -89,6 +89,17 @@ def parse():
     return ap.parse_args()
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(x, w, causal, budget_s: float):
     """Time the fp64 oracle, fwd + bwd, head by head until the budget is used."""
     import oracle   # test infrastructure: only this leg of the benchmark uses it
@@ -96,29 +107,34 @@ def cpu_baseline(x, w, causal, budget_s: float):
     cores = len(os.sched_getaffinity(0))
     torch.set_num_threads(cores)
     B, N, H, d = x["q"].shape
-    done, flops, t_total = 0, 0, 0.0
+    done, t_fwd, t_bwd = 0, 0.0, 0.0
     for b in range(B):
         for h in range(H):
             sl = (slice(b, b + 1), slice(None), slice(h, h + 1))
             q, k, v, do = (x[n][sl].contiguous() for n in ("q", "k", "v", "dout"))
             t0 = time.perf_counter()
             oracle.attention_forward(q, k, v, w.scale, causal)
+            t1 = time.perf_counter()
             oracle.attention_backward(q, k, v, do, w.scale, causal)
-            t_total += time.perf_counter() - t0
+            t_fwd += t1 - t0
+            t_bwd += time.perf_counter() - t1
             done += 1
-            p = acc.pairs(N, N, causal)
-            flops += acc.flops_fwd(p, d) + acc.flops_bwd(p, d)
-            if t_total >= budget_s:
+            if t_fwd + t_bwd >= budget_s:
                 break
-        if t_total >= budget_s:
+        if t_fwd + t_bwd >= budget_s:
             break
+    p = acc.pairs(N, N, causal) * done
+    f_fwd, f_bwd = acc.flops_fwd(p, d), acc.flops_bwd(p, d)
     return {
-        "value": round(flops / t_total / 1e12, 6),
+        "value": round((f_fwd + f_bwd) / (t_fwd + t_bwd) / 1e12, 6),
         "unit": "TFLOP/s",
         "cores": torch.get_num_threads(),
         "kind": "oracle",
         "sample": f"{done} of {B * H} (batch, head) slices, forward + backward, float64, "
-                  f"{t_total:.1f} s",
+                  f"{t_fwd + t_bwd:.1f} s",
+        "fwd_tflops": round(f_fwd / t_fwd / 1e12, 6),
+        "bwd_tflops": round(f_bwd / t_bwd / 1e12, 6),
+        "cpu": cpu_model(),
     }
 
 
@@ -176,8 +192,9 @@ def main():
             ev[s][i + 1].record()
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / args.steps
-    kern_ms = [sum(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(args.steps)) / args.steps
-               for i in range(len(calls))]
+    per_step = [[ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(args.steps)]
+                for i in range(len(calls))]
+    kern_ms = [sum(t) / len(t) for t in per_step]
 
     cnt = acc.dense_counts(B, H, N, d, causal)
     pairs = cnt["pairs"]
@@ -186,8 +203,9 @@ def main():
     kern_flops = [f_fwd, 0, 8 * d * pairs, 2 * d * pairs]
     dot_bytes = B * N * H * (2 * 2 * d + 4 + 8)   # O, dO, LSE in; -D, LSE*log2(e) out
     kern = {}
-    for n, ms, fl in zip(names, kern_ms, kern_flops):
-        e = {"ms": round(ms, 4)}
+    for n, ms, fl, ts in zip(names, kern_ms, kern_flops, per_step):
+        ts = sorted(ts)
+        e = {"ms": round(ms, 4), "ms_median": round(ts[len(ts) // 2], 4), "ms_min": round(ts[0], 4)}
         if fl:
             e["tflops"] = round(fl / (ms * 1e-3) / 1e12, 2)
         else:
