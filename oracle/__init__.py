@@ -18,6 +18,11 @@ Parity status of each function (what pins it, see ``tests/test_oracle_pins.py``)
   arbitrary key-block splits, and the pins above through that equality).
 * ``attention_forward_varlen`` / ``attention_backward_varlen``: pinned
   (per-sequence agreement with torch fp64 SDPA on each sequence).
+* ``decode_forward`` (grouped-query decoding): pinned (equals the dense
+  functions above on key/value heads expanded per group, torch fp64 SDPA with
+  an explicit bottom-right mask, one query token = no mask).
+* ``decode_split_partials`` / ``merge_splits``: pinned (any key split merged
+  equals the one-shot result; the merge is associative).
 """
 
 from .attention import (  # noqa: F401
@@ -27,4 +32,9 @@ from .attention import (  # noqa: F401
     online_softmax_forward,
     attention_forward_varlen,
     attention_backward_varlen,
+)
+from .decode import (  # noqa: F401
+    decode_forward,
+    decode_split_partials,
+    merge_splits,
 )
