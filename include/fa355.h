@@ -139,6 +139,29 @@ int fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o,
                   const int* cu_seqlens_k, int nseq, int max_seqlen_q, int max_seqlen_k,
                   int H, int d, float scale, int causal, void* stream);
 
+/*
+ * Decoding ("LLM Systems 22: Flash Attention", §5.1 Motivation, §5.2 Solution):
+ * Nq new query tokens per sequence (typically 1..4) against an Nk-token
+ * key/value cache, Hq query heads grouped onto Hkv key/value heads (query head
+ * h reads key/value head h / (Hq/Hkv)).  The keys are split into chunks
+ * processed in parallel (split-KV); each chunk's normalised output and
+ * log-sum-exp go to the workspace and a second kernel merges them.  The query
+ * heads of one group and the Nq tokens are packed into the rows of one matrix
+ * tile (GQA packing).
+ *   q [B,Nq,Hq,d], k, v [B,Nk,Hkv,d], o [B,Nq,Hq,d] bf16; lse [B,Hq,Nq] fp32,
+ *   natural log of the scaled scores.  d in {64,128}; Hkv must divide Hq.
+ *   causal: the Nq tokens are the newest positions, token i sees keys
+ *   j <= i + Nk - Nq (needs Nq <= Nk); otherwise every key.
+ *   workspace: at least fa_decode_workspace_bytes(...) bytes, 16-byte aligned,
+ *   contents irrelevant on entry and unspecified on return.
+ * Errors as fa_fwd; FA_ERR_WORKSPACE for a missing or small workspace,
+ * FA_ERR_UNSUPPORTED also when Nk * Hkv * d * 2 bytes reach 2 GiB.
+ */
+size_t fa_decode_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nk, int d);
+int fa_fwd_decode(const void* q, const void* k, const void* v, void* o, float* lse, void* workspace,
+                  size_t workspace_bytes, int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale,
+                  int causal, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

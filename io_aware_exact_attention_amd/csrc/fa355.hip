@@ -6,6 +6,7 @@
 // explicit error instead of falling back silently.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <climits>
 #include <cmath>
 #include <cstdint>
@@ -15,6 +16,7 @@
 
 #include "../../include/fa355.h"
 #include "fa_bwd.hpp"
+#include "fa_decode.hpp"
 #include "fa_fwd.hpp"
 
 using namespace fa355;
@@ -140,6 +142,33 @@ int launch_bwd(const AttnParams& p, int d, int causal, hipStream_t s, int stages
 void set_workspace(AttnParams& p, void* ws) {
     p.dvec = static_cast<float*>(ws);
     p.lse2 = p.dvec + (size_t)p.batch * p.H * p.nq;
+}
+
+// Decoding: split the keys so that about kDecodeWaves chunk waves run, each
+// chunk a multiple of the 32-key tile.  Everything the workspace size depends on
+// is derived here, from the shapes only.
+constexpr int kDecodeWaves = 1024;
+
+struct DecodePlan {
+    int G, rows, row_tiles, splits, split_len;
+    size_t opart_floats, lpart_floats;
+};
+
+DecodePlan decode_plan(int B, int Hq, int Hkv, int Nq, int Nk, int d) {
+    DecodePlan pl{};
+    pl.G = Hq / Hkv;
+    pl.rows = pl.G * Nq;
+    pl.row_tiles = (pl.rows + 31) / 32;
+    const int64_t units = (int64_t)B * Hkv * pl.row_tiles;
+    const int64_t want = std::max<int64_t>(1, (kDecodeWaves + units - 1) / units);
+    int64_t len = (Nk + want - 1) / want;
+    len = std::max<int64_t>(32, (len + 31) / 32 * 32);
+    pl.split_len = (int)len;
+    pl.splits = (int)((Nk + len - 1) / len);
+    const size_t slots = (size_t)B * Hkv * pl.row_tiles * 32 * pl.splits;
+    pl.opart_floats = slots * d;
+    pl.lpart_floats = slots;
+    return pl;
 }
 
 AttnParams base_params(const void* q, const void* k, const void* v, int batch, int H, int nq,
@@ -354,6 +383,74 @@ int fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o, co
     p.cu_q = cu_seqlens_q;
     p.cu_k = cu_seqlens_k;
     return launch_bwd<true>(p, d, causal, s);
+}
+
+size_t fa_decode_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nk, int d) {
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || Nq <= 0 || Nk <= 0 || Hq % Hkv != 0 || (d != 64 && d != 128))
+        return 0;
+    const DecodePlan pl = decode_plan(B, Hq, Hkv, Nq, Nk, d);
+    return sizeof(float) * (pl.opart_floats + pl.lpart_floats);
+}
+
+int fa_fwd_decode(const void* q, const void* k, const void* v, void* o, float* lse, void* workspace,
+                  size_t workspace_bytes, int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale,
+                  int causal, void* stream) {
+    if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+    if (B <= 0 || Nq <= 0 || Nk <= 0 || Hkv <= 0) return FA_ERR_SHAPE;
+    int st = check_common(Hq, d, scale, causal);
+    if (st) return st;
+    if (Hq % Hkv != 0) return FA_ERR_SHAPE;
+    if (causal && Nq > Nk) return FA_ERR_UNSUPPORTED;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4) ||
+        !aligned(workspace, 16))
+        return FA_ERR_ALIGN;
+    const size_t need = fa_decode_workspace_bytes(B, Hq, Hkv, Nq, Nk, d);
+    if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
+    // one sequence's cache rows of one tensor go through a buffer resource (< 2 GiB)
+    if ((int64_t)Nk * Hkv * d * 2 >= ((int64_t)1 << 31)) return FA_ERR_UNSUPPORTED;
+    const int64_t lim = (int64_t)1 << 40;
+    if ((int64_t)B * Nq * Hq * d > lim || (int64_t)B * Nk * Hkv * d > lim) return FA_ERR_SHAPE;
+    const DecodePlan pl = decode_plan(B, Hq, Hkv, Nq, Nk, d);
+    const int64_t grid1 = (int64_t)B * Hkv * pl.row_tiles * pl.splits;
+    const int64_t grid2 = (int64_t)B * Hkv * pl.rows;
+    if (grid1 > INT_MAX || grid2 > INT_MAX) return FA_ERR_SHAPE;
+    DecodeParams p;
+    std::memset(&p, 0, sizeof(p));
+    p.q = static_cast<const bf16*>(q);
+    p.k = static_cast<const bf16*>(k);
+    p.v = static_cast<const bf16*>(v);
+    p.o = static_cast<bf16*>(o);
+    p.lse = lse;
+    p.opart = static_cast<float*>(workspace);
+    p.lpart = p.opart + pl.opart_floats;
+    p.B = B;
+    p.Nq = Nq;
+    p.Nk = Nk;
+    p.Hq = Hq;
+    p.Hkv = Hkv;
+    p.G = pl.G;
+    p.rows = pl.rows;
+    p.row_tiles = pl.row_tiles;
+    p.splits = pl.splits;
+    p.split_len = pl.split_len;
+    p.scale = scale;
+    p.scale_log2 = scale * kLog2e;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    void* args[] = {&p};
+    const void* k1;
+    const void* k2;
+    if (d == 64) {
+        k1 = causal ? reinterpret_cast<const void*>(fa_decode_split_kernel<64, true>)
+                    : reinterpret_cast<const void*>(fa_decode_split_kernel<64, false>);
+        k2 = reinterpret_cast<const void*>(fa_decode_combine_kernel<64>);
+    } else {
+        k1 = causal ? reinterpret_cast<const void*>(fa_decode_split_kernel<128, true>)
+                    : reinterpret_cast<const void*>(fa_decode_split_kernel<128, false>);
+        k2 = reinterpret_cast<const void*>(fa_decode_combine_kernel<128>);
+    }
+    if (hipLaunchKernel(k1, dim3((unsigned)grid1), dim3(64), args, 0, s) != hipSuccess) return FA_ERR_LAUNCH;
+    if (hipLaunchKernel(k2, dim3((unsigned)grid2), dim3(d), args, 0, s) != hipSuccess) return FA_ERR_LAUNCH;
+    return FA_OK;
 }
 
 }  // extern "C"

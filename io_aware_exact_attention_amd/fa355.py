@@ -36,6 +36,8 @@ _SIGNATURES = {
     "fa_bwd_dot": (_c_int, [_vp] * 4 + [_sz] + [_c_int] * 4 + [_vp]),
     "fa_bwd_dkdv": (_c_int, [_vp] * 5 + [_sz] + [_vp] * 2 + [_c_int] * 5 + [_c_float, _c_int, _vp]),
     "fa_bwd_dq": (_c_int, [_vp] * 5 + [_sz] + [_vp] + [_c_int] * 5 + [_c_float, _c_int, _vp]),
+    "fa_decode_workspace_bytes": (_sz, [_c_int] * 6),
+    "fa_fwd_decode": (_c_int, [_vp] * 6 + [_sz] + [_c_int] * 6 + [_c_float, _c_int, _vp]),
 }
 
 STATUS = {0: "FA_OK", -1: "FA_ERR_NULL", -2: "FA_ERR_SHAPE", -3: "FA_ERR_UNSUPPORTED",
@@ -159,6 +161,20 @@ def fa_bwd_varlen(q, k, v, o, dout, lse, dq, dk, dv, workspace, cu_seqlens_q, cu
                                int(bool(causal)), _stream(stream)))
 
 
+def fa_decode_workspace_bytes(B: int, Hq: int, Hkv: int, Nq: int, Nk: int, d: int) -> int:
+    return int(lib().fa_decode_workspace_bytes(int(B), int(Hq), int(Hkv), int(Nq), int(Nk), int(d)))
+
+
+def fa_fwd_decode(q, k, v, o, lse, workspace, scale: float, causal: bool, stream=None):
+    """q [B,Nq,Hq,d]; k, v [B,Nk,Hkv,d]; o like q; lse [B,Hq,Nq] fp32."""
+    B, Nq, Hq, d = q.shape
+    Nk, Hkv = k.shape[1], k.shape[2]
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(lib().fa_fwd_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(workspace),
+                               nbytes, B, Hq, Hkv, Nq, Nk, d, float(scale), int(bool(causal)),
+                               _stream(stream)))
+
+
 # ---------------------------------------------------------------------------
 # conveniences: allocate outputs (device memory via torch), then call the ABI
 
@@ -200,3 +216,15 @@ def attention_backward_varlen(q, k, v, o, dout, lse, cu_seqlens_q, cu_seqlens_k,
     fa_bwd_varlen(q, k, v, o, dout, lse, dq, dk, dv, workspace, cu_seqlens_q, cu_seqlens_k,
                   max_seqlen_q, max_seqlen_k, scale, causal)
     return dq, dk, dv
+
+
+def attention_decode(q, k, v, scale: float, causal: bool, workspace=None):
+    B, Nq, Hq, d = q.shape
+    Nk, Hkv = k.shape[1], k.shape[2]
+    o = torch.empty_like(q)
+    lse = torch.empty(B, Hq, Nq, dtype=torch.float32, device=q.device)
+    if workspace is None:
+        nbytes = fa_decode_workspace_bytes(B, Hq, Hkv, Nq, Nk, d)
+        workspace = torch.empty(max(nbytes, 16) // 4, dtype=torch.float32, device=q.device)
+    fa_fwd_decode(q, k, v, o, lse, workspace, scale, causal)
+    return o, lse

@@ -10,7 +10,8 @@ Recipe (identical for every consumer):
   * one round-to-nearest-even conversion to bf16 (k is multiplied by
     ``k_scale`` in fp32 before that single rounding, for peaky rows);
   * packed batches: sequence lengths drawn first, from numpy's
-    ``default_rng(seed)``, uniform integers in [min_len, max_len] inclusive.
+    ``default_rng(seed)``, uniform integers in [min_len, max_len] inclusive;
+  * decoding workloads draw q, k, v only (k and v have the key/value heads).
 
 Dense tensors are [B, N, H, d]; packed tensors are [total, H, d].
 """
@@ -71,6 +72,36 @@ WORKLOADS = {
 HEADLINE = "b8_h16_n4096_d128_causal"
 
 
+@dataclasses.dataclass(frozen=True)
+class DecodeWorkload:
+    """Decoding: Nq new query tokens per sequence against an Nk-token key/value
+    cache, Hq query heads sharing Hkv key/value heads (grouped-query)."""
+    name: str
+    B: int
+    Nq: int
+    Nk: int
+    Hq: int
+    Hkv: int
+    d: int
+    causal: bool
+    seed: int
+    note: str = ""
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+
+DECODE_WORKLOADS = {
+    w.name: w
+    for w in (
+        DecodeWorkload("decode_b2_hq32_hkv4_nq4_nk131072_d128", B=2, Nq=4, Nk=131072, Hq=32, Hkv=4,
+                       d=128, causal=True, seed=1006,
+                       note="4 new tokens against a 128k-token cache, 8 query heads per KV head"),
+    )
+}
+
+
 def seq_lengths(nseq: int, min_len: int, max_len: int, seed: int) -> list[int]:
     """Sequence lengths, uniform integers in [min_len, max_len] inclusive."""
     rng = np.random.default_rng(seed)
@@ -127,8 +158,19 @@ def make_packed(lengths, H: int, d: int, seed: int, with_dout: bool = True) -> d
     return out
 
 
+def make_decode(B: int, Nq: int, Nk: int, Hq: int, Hkv: int, d: int, seed: int) -> dict:
+    """bf16 q [B,Nq,Hq,d], k/v [B,Nk,Hkv,d] from one seeded stream (draws q, k, v)."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed))
+    return {"q": _draw(g, (B, Nq, Hq, d)), "k": _draw(g, (B, Nk, Hkv, d)),
+            "v": _draw(g, (B, Nk, Hkv, d))}
+
+
 def make_inputs(name: str, with_dout: bool = True) -> dict:
     """Inputs of a named workload (CPU, bf16)."""
+    if name in DECODE_WORKLOADS:
+        w = DECODE_WORKLOADS[name]
+        return make_decode(w.B, w.Nq, w.Nk, w.Hq, w.Hkv, w.d, w.seed)
     w = WORKLOADS[name]
     if w.varlen:
         lens = seq_lengths(w.nseq, w.min_len, w.max_len, w.seed)

@@ -111,6 +111,33 @@ def test_stage_entry_points_reject():
     assert lib.fa_bwd_dq(*[A] * 4, A, W, A, 1, 1, 0, 16, 64, 0.1, 0, None) == -2
 
 
+def test_decode_rejects():
+    lib = fa355.lib()
+    W = 1 << 30
+
+    def dec(q=A, k=A, v=A, o=A, lse=A, ws=A, wsb=W, B=1, Hq=8, Hkv=2, Nq=4, Nk=100, d=128,
+            scale=0.1, causal=1):
+        return lib.fa_fwd_decode(q, k, v, o, lse, ws, wsb, B, Hq, Hkv, Nq, Nk, d, scale, causal, None)
+
+    assert dec(q=None) == -1 and dec(lse=None) == -1
+    assert dec(B=0) == -2 and dec(Nq=0) == -2 and dec(Nk=0) == -2 and dec(Hkv=0) == -2
+    assert dec(Hq=6, Hkv=4) == -2                       # Hkv must divide Hq
+    assert dec(d=96) == -3 and dec(scale=0.0) == -3
+    assert dec(Nq=8, Nk=4, causal=1) == -3              # causal needs Nq <= Nk
+    assert dec(Nq=8, Nk=4, causal=0, ws=None) == -6     # non-causal is fine, workspace is not
+    assert dec(ws=None) == -6 and dec(wsb=16) == -6
+    assert dec(k=MIS) == -4 and dec(ws=A + 4) == -4
+    assert dec(Hkv=64, Hq=64, Nk=1 << 17) == -3         # one sequence's cache rows span 2 GiB
+
+
+def test_decode_workspace_bytes():
+    n = fa355.fa_decode_workspace_bytes(2, 32, 4, 4, 131072, 128)
+    # two planes of slots (B * Hkv * 32 rows * splits): outputs (d floats) and LSEs
+    assert n > 0 and n % (4 * 129) == 0
+    assert fa355.fa_decode_workspace_bytes(2, 30, 4, 4, 100, 128) == 0
+    assert fa355.fa_decode_workspace_bytes(0, 32, 4, 4, 100, 128) == 0
+
+
 def test_binding_raises_on_error():
     with pytest.raises(fa355.FaError) as e:
         fa355._check(-3)
