@@ -138,6 +138,99 @@ def cpu_baseline(x, w, causal, budget_s: float):
     }
 
 
+DECODE_METRIC = "split-KV decode HBM GB/s, % of 8 TB/s"
+
+
+def decode_cpu_baseline(x, w, budget_s: float):
+    """Time the fp64 decoding oracle one (sequence, key/value head) group at a time."""
+    import oracle   # test infrastructure: only this leg of the benchmark uses it
+
+    torch.set_num_threads(len(os.sched_getaffinity(0)))
+    G = w.Hq // w.Hkv
+    done, t_total, nbytes = 0, 0.0, 0
+    for b in range(w.B):
+        for hk in range(w.Hkv):
+            hs = slice(hk * G, (hk + 1) * G)
+            q = x["q"][b:b + 1, :, hs].contiguous()
+            k = x["k"][b:b + 1, :, hk:hk + 1].contiguous()
+            v = x["v"][b:b + 1, :, hk:hk + 1].contiguous()
+            t0 = time.perf_counter()
+            oracle.decode_forward(q, k, v, w.scale, w.causal)
+            t_total += time.perf_counter() - t0
+            done += 1
+            nbytes += 2 * w.Nk * w.d * 2
+            if t_total >= budget_s:
+                break
+        if t_total >= budget_s:
+            break
+    return {"value": round(nbytes / t_total / 1e9, 4), "unit": "GB/s",
+            "cores": torch.get_num_threads(), "kind": "oracle",
+            "sample": f"{done} of {w.B * w.Hkv} (sequence, key/value head) groups, float64, "
+                      f"{t_total:.1f} s",
+            "cpu": cpu_model()}
+
+
+def run_decode(args, w):
+    """Decoding workload: one step = fa_fwd_decode (split kernel + merge kernel)."""
+    dev = torch.device("cuda", 0)
+    x = wl.make_inputs(w.name)
+    q, k, v = (x[n].to(dev) for n in ("q", "k", "v"))
+    o = torch.empty_like(q)
+    lse = torch.empty(w.B, w.Hq, w.Nq, dtype=torch.float32, device=dev)
+    nbytes = fa355.fa_decode_workspace_bytes(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.d)
+    ws = torch.empty(nbytes // 4, dtype=torch.float32, device=dev)
+    call = lambda: fa355.fa_fwd_decode(q, k, v, o, lse, ws, w.scale, w.causal)
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    t0 = time.perf_counter()
+    ev[0].record()
+    for s in range(args.steps):
+        call()
+        ev[s + 1].record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / args.steps
+    ts = sorted(ev[s].elapsed_time(ev[s + 1]) for s in range(args.steps))
+    ms = sum(ts) / len(ts)
+    # compulsory bytes: the cache once, q in, o and lse out
+    kv_bytes = 2 * w.B * w.Nk * w.Hkv * w.d * 2
+    io_bytes = kv_bytes + 2 * w.B * w.Nq * w.Hq * w.d * 2 + w.B * w.Hq * w.Nq * 4
+    pairs = w.B * w.Hq * sum(min(w.Nk, i + w.Nk - w.Nq + 1) if w.causal else w.Nk
+                              for i in range(w.Nq))
+    gbs = io_bytes / (ms * 1e-3) / 1e9
+    out = {
+        "metric": DECODE_METRIC,
+        "value": round(io_bytes / wall / 1e9, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "Nq": w.Nq, "Nk": w.Nk, "Hq": w.Hq,
+                   "Hkv": w.Hkv, "d": w.d, "causal": w.causal, "scale": w.scale},
+        "decode": {"ms": round(ms, 4), "ms_median": round(ts[len(ts) // 2], 4),
+                   "ms_min": round(ts[0], 4), "gbs": round(gbs, 1),
+                   "tflops": round(4 * w.d * pairs / (ms * 1e-3) / 1e12, 3),
+                   "algorithmic_bytes": io_bytes,
+                   "workspace_bytes": nbytes},
+        # events bracket both kernels of the entry point (split + merge); the
+        # kernel-trace summary in profiles/ separates them
+        "roofline": {"kernel": "fa_decode_split_kernel + fa_decode_combine_kernel",
+                     "bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                     "algorithmic_bytes": io_bytes},
+        "device": torch.cuda.get_device_name(0),
+    }
+    out["cpu_baseline"] = decode_cpu_baseline(x, w, args.cpu_seconds) if args.cpu_seconds > 0 else None
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -147,6 +240,8 @@ def main():
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
+    if args.workload in wl.DECODE_WORKLOADS:
+        return run_decode(args, wl.DECODE_WORKLOADS[args.workload])
     w = wl.WORKLOADS[args.workload]
     if w.varlen:
         raise SystemExit("bench.py times the dense workloads")

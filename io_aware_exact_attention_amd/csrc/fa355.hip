@@ -147,7 +147,7 @@ void set_workspace(AttnParams& p, void* ws) {
 // Decoding: split the keys so that about kDecodeWaves chunk waves run, each
 // chunk a multiple of the 32-key tile.  Everything the workspace size depends on
 // is derived here, from the shapes only.
-constexpr int kDecodeWaves = 1024;
+constexpr int kDecodeWaves = kDecodeMaxSplits;
 
 struct DecodePlan {
     int G, rows, row_tiles, splits, split_len;
@@ -164,7 +164,7 @@ DecodePlan decode_plan(int B, int Hq, int Hkv, int Nq, int Nk, int d) {
     int64_t len = (Nk + want - 1) / want;
     len = std::max<int64_t>(32, (len + 31) / 32 * 32);
     pl.split_len = (int)len;
-    pl.splits = (int)((Nk + len - 1) / len);
+    pl.splits = (int)((Nk + len - 1) / len);   // <= kDecodeWaves = kDecodeMaxSplits
     const size_t slots = (size_t)B * Hkv * pl.row_tiles * 32 * pl.splits;
     pl.opart_floats = slots * d;
     pl.lpart_floats = slots;

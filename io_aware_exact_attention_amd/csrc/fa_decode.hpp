@@ -209,31 +209,69 @@ __global__ __launch_bounds__(64) void fa_decode_split_kernel(DecodeParams p) {
     }
 }
 
-// Merge of the chunk results of one packed row: one thread per output element.
+// Merge of the chunk results of one packed row.  One thread per output element;
+// the chunk LSEs are first staged in LDS and reduced by the whole work-group
+// (max, then the sum of e^(LSE_s - max)), so that the per-element pass only
+// streams the chunk outputs, several loads in flight per thread.
+constexpr int kDecodeMaxSplits = 1024;
+
 template <int D>
 __global__ __launch_bounds__(D) void fa_decode_combine_kernel(DecodeParams p) {
+    __shared__ float wgt[kDecodeMaxSplits];
+    __shared__ float red[D / 64];
     int idx = blockIdx.x;
     const int pr = idx % p.rows;
     idx /= p.rows;
     const int hkv = idx % p.Hkv;
     const int b = idx / p.Hkv;
     const int dim = threadIdx.x;
+    const int lane = threadIdx.x & 63;
+    const int wv = threadIdx.x >> 6;
     const int tq = pr % p.Nq;
     const int hq = hkv * p.G + pr / p.Nq;
     const int64_t slot0 = ((int64_t)(b * p.Hkv + hkv) * p.row_tiles * 32 + pr) * p.splits;
     const float* lp = p.lpart + slot0;
 
     float top = kNegInf;
-    for (int s = 0; s < p.splits; ++s) top = fmaxf(top, lp[s]);
+    for (int s = dim; s < p.splits; s += D) {
+        const float x = lp[s];
+        wgt[s] = x;
+        top = fmaxf(top, x);
+    }
+#pragma unroll
+    for (int w = 32; w > 0; w >>= 1) top = fmaxf(top, __shfl_xor(top, w));
+    if (lane == 0) red[wv] = top;
+    __syncthreads();
+    top = red[0];
+#pragma unroll
+    for (int i = 1; i < D / 64; ++i) top = fmaxf(top, red[i]);
     const float base = top == kNegInf ? 0.f : top;
+    __syncthreads();   // everyone has read red[] before it is reused
+    float part = 0.f;
+    for (int s = dim; s < p.splits; s += D) {
+        const float e = fast_exp2((wgt[s] - base) * kLog2e);   // -inf chunks -> 0
+        wgt[s] = e;
+        part += e;
+    }
+#pragma unroll
+    for (int w = 32; w > 0; w >>= 1) part += __shfl_xor(part, w);
+    if (lane == 0) red[wv] = part;
+    __syncthreads();
     float tot = 0.f;
-    for (int s = 0; s < p.splits; ++s) tot += fast_exp2((lp[s] - base) * kLog2e);
+#pragma unroll
+    for (int i = 0; i < D / 64; ++i) tot += red[i];
     const float inv = tot > 0.f ? 1.f / tot : 0.f;
+
     const float* op = p.opart + slot0 * D + dim;
-    float acc = 0.f;
-    for (int s = 0; s < p.splits; ++s)
-        acc = __builtin_fmaf(fast_exp2((lp[s] - base) * kLog2e) * inv, op[(int64_t)s * D], acc);
-    p.o[((int64_t)(b * p.Nq + tq) * p.Hq + hq) * D + dim] = (bf16)acc;
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    int s = 0;
+    for (; s + 4 <= p.splits; s += 4) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) acc[u] = __builtin_fmaf(wgt[s + u], op[(int64_t)(s + u) * D], acc[u]);
+    }
+    for (; s < p.splits; ++s) acc[0] = __builtin_fmaf(wgt[s], op[(int64_t)s * D], acc[0]);
+    const float o = ((acc[0] + acc[1]) + (acc[2] + acc[3])) * inv;
+    p.o[((int64_t)(b * p.Nq + tq) * p.Hq + hq) * D + dim] = (bf16)o;
     if (dim == 0)
         p.lse[((int64_t)b * p.Hq + hq) * p.Nq + tq] = tot > 0.f ? base + __builtin_amdgcn_logf(tot) * kLn2 : kNegInf;
 }
