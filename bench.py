@@ -89,6 +89,16 @@ def parse():
     return ap.parse_args()
 
 
+def calibration_copy(dev):
+    """One plain device copy of known size, outside the timed region: under
+    rocprofv3 --pmc its FETCH_SIZE / WRITE_SIZE calibrate the byte counters."""
+    calib = torch.empty(CALIB_BYTES // 2, dtype=torch.bfloat16, device=dev)
+    calib_dst = torch.empty_like(calib)
+    calib_dst.copy_(calib)
+    del calib, calib_dst
+    torch.cuda.synchronize()
+
+
 def cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as f:
@@ -180,6 +190,7 @@ def run_decode(args, w):
     nbytes = fa355.fa_decode_workspace_bytes(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.d)
     ws = torch.empty(nbytes // 4, dtype=torch.float32, device=dev)
     call = lambda: fa355.fa_fwd_decode(q, k, v, o, lse, ws, w.scale, w.causal)
+    calibration_copy(dev)
     for _ in range(args.warmup):
         call()
     torch.cuda.synchronize()
@@ -199,6 +210,7 @@ def run_decode(args, w):
     pairs = w.B * w.Hq * sum(min(w.Nk, i + w.Nk - w.Nq + 1) if w.causal else w.Nk
                               for i in range(w.Nq))
     gbs = io_bytes / (ms * 1e-3) / 1e9
+    traffic = measured_traffic(w.name)
     out = {
         "metric": DECODE_METRIC,
         "value": round(io_bytes / wall / 1e9, 1),
@@ -223,7 +235,9 @@ def run_decode(args, w):
         # kernel-trace summary in profiles/ separates them
         "roofline": {"kernel": "fa_decode_split_kernel + fa_decode_combine_kernel",
                      "bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
-                     "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                     "traffic": (traffic.get("fa_decode_split_kernel", 0) +
+                                 traffic.get("fa_decode_combine_kernel", 0)) if traffic else None,
                      "algorithmic_bytes": io_bytes},
         "device": torch.cuda.get_device_name(0),
     }
@@ -263,13 +277,7 @@ def main():
         lambda: fa355.fa_bwd_dkdv(q, k, v, do, ws, dk, dv, scale, causal),
         lambda: fa355.fa_bwd_dq(q, k, v, do, ws, dq, scale, causal),
     ]
-    # One plain device copy of known size, outside the timed region: under
-    # rocprofv3 --pmc its FETCH_SIZE / WRITE_SIZE calibrate the byte counters.
-    calib = torch.empty(CALIB_BYTES // 2, dtype=torch.bfloat16, device=dev)
-    calib_dst = torch.empty_like(calib)
-    calib_dst.copy_(calib)
-    del calib, calib_dst
-    torch.cuda.synchronize()
+    calibration_copy(dev)
 
     for _ in range(args.warmup):
         for c in calls:
