@@ -245,6 +245,76 @@ def run_decode(args, w):
     print(json.dumps(out), flush=True)
 
 
+def run_varlen(args, w):
+    """Packed variable-length workload: one step = fa_fwd_varlen + fa_bwd_varlen."""
+    dev = torch.device("cuda", 0)
+    x = wl.make_inputs(w.name)
+    q, k, v, do = (x[n].to(dev) for n in ("q", "k", "v", "dout"))
+    cu = x["cu_seqlens"].to(dev)
+    mx = x["max_seqlen"]
+    nseq = cu.numel() - 1
+    causal = w.causal[-1]
+    o = torch.empty_like(q)
+    lse = torch.empty(nseq, w.H, mx, dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(fa355.fa_bwd_workspace_bytes(nseq, w.H, mx, w.d) // 4, dtype=torch.float32,
+                     device=dev)
+    calls = [
+        lambda: fa355.fa_fwd_varlen(q, k, v, o, lse, cu, cu, mx, mx, w.scale, causal),
+        lambda: fa355.fa_bwd_varlen(q, k, v, o, do, lse, dq, dk, dv, ws, cu, cu, mx, mx, w.scale,
+                                    causal),
+    ]
+    calibration_copy(dev)
+    for _ in range(args.warmup):
+        for c in calls:
+            c()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        ev[s][0].record()
+        for i, c in enumerate(calls):
+            c()
+            ev[s][i + 1].record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / args.steps
+    t_fwd = sum(ev[s][0].elapsed_time(ev[s][1]) for s in range(args.steps)) / args.steps
+    t_bwd = sum(ev[s][1].elapsed_time(ev[s][2]) for s in range(args.steps)) / args.steps
+    cnt = acc.varlen_counts(x["lengths"], w.H, w.d, causal)
+    f_fwd, f_bwd = cnt["flops_fwd"], cnt["flops_bwd"]
+    fwd_tf = f_fwd / (t_fwd * 1e-3) / 1e12
+    value = (f_fwd + f_bwd) / wall / 1e12
+    out = {
+        "metric": METRIC.replace("B8 H16 N4096 d128 causal", "packed varlen"),
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "H": w.H, "d": w.d, "nseq": nseq,
+                   "tokens": int(sum(x["lengths"])), "max_seqlen": mx, "causal": causal},
+        "fwd_ms": round(t_fwd, 4),
+        "bwd_ms": round(t_bwd, 4),
+        "fwd_tflops": round(fwd_tf, 2),
+        "fwd_pct_peak": round(100 * fwd_tf / PEAK_BF16_TFLOPS, 2),
+        "bwd_tflops": round(f_bwd / (t_bwd * 1e-3) / 1e12, 2),
+        "fwd_bwd_pct_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "fwd_hbm_gbs": round(cnt["bytes_fwd"] / (t_fwd * 1e-3) / 1e9, 1),
+        "roofline": {"kernel": "fa_fwd_kernel + fa_bwd_* (varlen)", "bound": "mfma",
+                     "achieved": round(value, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(value / PEAK_BF16_TFLOPS, 4), "traffic": None},
+        "device": torch.cuda.get_device_name(0),
+        "cpu_baseline": None,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -258,7 +328,7 @@ def main():
         return run_decode(args, wl.DECODE_WORKLOADS[args.workload])
     w = wl.WORKLOADS[args.workload]
     if w.varlen:
-        raise SystemExit("bench.py times the dense workloads")
+        return run_varlen(args, w)
     causal = w.causal[-1]
     dev = torch.device("cuda", 0)
     x = wl.make_inputs(w.name)

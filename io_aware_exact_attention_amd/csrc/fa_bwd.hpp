@@ -132,9 +132,8 @@ void fa_bwd_dkdv_kernel(AttnParams p) {
     const int sl = lane & 15;
     const int g = (lane >> 4) & 1;
 
-    const int L = xcd_logical_index(blockIdx.x, gridDim.x);
-    const int tile = L % p.n_tiles;        // low key tiles see the most query rows: first
-    const int bh = L / p.n_tiles;
+    int bh, tile;   // low key tiles see the most query rows: first
+    xcd_work_item(blockIdx.x, p.n_tiles, p.H * p.batch, bh, tile);
     const int h = bh % p.H;
     const int b = bh / p.H;
     int qs, nq, ks, nk;
@@ -304,9 +303,9 @@ void fa_bwd_dq_kernel(AttnParams p) {
     const int sl = lane & 15;
     const int g = (lane >> 4) & 1;
 
-    const int L = xcd_logical_index(blockIdx.x, gridDim.x);
-    const int tile = p.n_tiles - 1 - (L % p.n_tiles);
-    const int bh = L / p.n_tiles;
+    int bh, rank;
+    xcd_work_item(blockIdx.x, p.n_tiles, p.H * p.batch, bh, rank);
+    const int tile = p.n_tiles - 1 - rank;
     const int h = bh % p.H;
     const int b = bh / p.H;
     int qs, nq, ks, nk;

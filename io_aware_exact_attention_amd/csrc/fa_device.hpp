@@ -113,13 +113,26 @@ __device__ __forceinline__ int lane_x4_here() {
     return v;
 }
 
-// Work-item order over a 1-D grid of `total` work-groups.  Consecutive
-// work-group ids are spread round-robin over the 8 XCDs (each with its own L2);
-// this maps XCD x to the contiguous logical range [x*total/8, (x+1)*total/8), so
-// the work-groups resident on one XCD share the same few heads' K/V in L2.
-__device__ __forceinline__ int xcd_logical_index(int id, int total) {
-    if ((total & 7) != 0) return id;
-    return (id & 7) * (total >> 3) + (id >> 3);
+// Work item of work-group `id` in a 1-D grid of n_tiles * bh_count work-groups:
+// the (batch or sequence, head) pair `bh` and the tile rank within that pair.
+// The hardware deals consecutive work-group ids round-robin to the 8 XCDs, each
+// with its own L2.  When bh_count is a multiple of 8, XCD x gets the pairs
+// bh = x, x + 8, x + 16, ... -- every XCD a share of every sequence, so unequal
+// sequence lengths do not unbalance the XCDs -- and each pair's tiles run
+// consecutively there, sharing that pair's K/V in the XCD's L2.  Otherwise
+// XCD x gets a contiguous range of the logical order (or, if the grid is not a
+// multiple of 8, the plain order).
+__device__ __forceinline__ void xcd_work_item(int id, int n_tiles, int bh_count, int& bh, int& rank) {
+    const int total = n_tiles * bh_count;
+    if ((bh_count & 7) == 0) {
+        const int j = id >> 3;
+        bh = (j / n_tiles) * 8 + (id & 7);
+        rank = j % n_tiles;
+        return;
+    }
+    const int L = (total & 7) == 0 ? (id & 7) * (total >> 3) + (id >> 3) : id;
+    bh = L / n_tiles;
+    rank = L % n_tiles;
 }
 
 }  // namespace fa355

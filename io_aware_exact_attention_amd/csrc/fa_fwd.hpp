@@ -56,9 +56,9 @@ void fa_fwd_kernel(AttnParams p) {
     const int h2 = lane >> 5;
     const int col = lane & 31;
 
-    const int L = xcd_logical_index(blockIdx.x, gridDim.x);
-    const int tile = p.n_tiles - 1 - (L % p.n_tiles);   // longest causal rows first
-    const int bh = L / p.n_tiles;
+    int bh, rank;
+    xcd_work_item(blockIdx.x, p.n_tiles, p.H * p.batch, bh, rank);
+    const int tile = p.n_tiles - 1 - rank;   // longest causal rows first
     const int h = bh % p.H;
     const int b = bh / p.H;
     int qs, nq, ks, nk;
