@@ -1,0 +1,292 @@
+"""FP8 (e4m3) attention forward with a random Hadamard rotation of Q and K, float64 on the CPU.
+
+TEST INFRASTRUCTURE (see the package docstring): only the tests, the smoke
+check and the CPU-baseline leg of the benchmark use this module.
+
+Sources (page title, then the section on that page):
+
+* The low-precision forward and its outlier remedy: Q and K are multiplied by a
+  random orthogonal matrix J (J J^T = I), which leaves S = Q K^T = (QJ)(KJ)^T
+  unchanged while spreading outliers concentrated in a few dimensions over all
+  of them, so that FP8 quantisation loses less: "LLM Systems 22: Flash
+  Attention", §4.1.3 Low-precision - FP8.  The page names the Hadamard
+  transform as J.
+* Everything after quantisation is the definition of attention with the safe
+  softmax and LSE = m + ln(l): "08 · FlashAttention", §一 and §二; "LLM Systems
+  22: Flash Attention", §3.2.
+
+Readings taken where the pages are silent (each one is a choice, stated):
+
+* Format: the pages say "FP8"; read as the OCP 8-bit E4M3 format (1 sign bit,
+  4 exponent bits with bias 7, 3 mantissa bits, subnormals, largest finite
+  value 448, no infinities, S.1111.111 is NaN).  Encoding rounds to nearest,
+  ties to the even code, and saturates at +-448.
+* J = diag(sigma) H_d / sqrt(d): H_d is the Sylvester Hadamard matrix
+  (H[i, j] = (-1)^popcount(i & j)) and sigma in {+1, -1}^d are random signs,
+  an input.  The rotated tensors are kept unnormalised, Qh = Q diag(sigma) H_d
+  (likewise Kh), and the 1/d that restores J's normalisation goes into the
+  score scale: Qh Kh^T = d Q K^T.  V is not rotated.
+* Scales: one per (batch, head) and tensor, a power of two,
+  s = 2^ceil(log2(amax / 448)) over that head's rotated values (s = 1 when
+  amax = 0); codes = e4m3(x / s).  Dividing by a power of two is exact, so the
+  code depends only on the value x.
+* Scores S = scale * s_q * s_k / d * (q8 . k8), decoded codes.
+* P~ = exp(S - m) lies in [0, 1]; the P V product uses p8 = e4m3(256 * P~)
+  and O = s_v / 256 * sum_j p8_j v8_j / l, where l = sum_j P~_j is the
+  unquantised row sum; LSE = m + ln(l).  m is the online softmax's running
+  maximum over blocks of 64 keys ("08 · FlashAttention", §二), so P~ is rounded
+  relative to the maximum seen so far and earlier blocks are rescaled after
+  rounding: the one-pass kernel cannot know the final maximum when it rounds.
+
+Layout: q, k, v [B, N, H, d]; codes the same, uint8; scales [B, H]; O
+[B, Nq, H, d]; LSE [B, H, Nq].
+"""
+
+from __future__ import annotations
+
+import math
+
+import torch
+
+_NEG_INF = float("-inf")
+E4M3_MAX = 448.0
+P_SCALE = 256.0          # P~ in [0, 1] is quantised as e4m3(256 * P~)
+KEY_BLOCK = 64           # keys per block of the online pass (the kernel's key tile)
+
+
+def _f64(x: torch.Tensor) -> torch.Tensor:
+    return x.detach().to(device="cpu", dtype=torch.float64)
+
+
+# --------------------------------------------------------------------- e4m3 codec
+
+def e4m3_decode(codes: torch.Tensor) -> torch.Tensor:
+    """Value of each code: (-1)^s 2^(e-7) (1 + m/8), subnormal (e = 0) 2^-6 m/8."""
+    c = codes.to(torch.int64)
+    s = (c >> 7) & 1
+    e = (c >> 3) & 15
+    m = (c & 7).to(torch.float64)
+    normal = torch.ldexp(1.0 + m / 8.0, (e - 7).to(torch.float64))
+    sub = torch.ldexp(m / 8.0, torch.full_like(m, -6.0))
+    v = torch.where(e == 0, sub, normal)
+    v = torch.where((e == 15) & ((c & 7) == 7), torch.full_like(v, float("nan")), v)
+    return torch.where(s == 1, -v, v)
+
+
+def _binade(a: torch.Tensor) -> torch.Tensor:
+    """floor(log2(a)) for a > 0, exactly (from the binary exponent); -6 for a = 0."""
+    _, ex = torch.frexp(torch.where(a > 0, a, torch.ones_like(a)))
+    return torch.where(a > 0, (ex - 1).to(torch.float64), torch.full_like(a, -6.0))
+
+
+def e4m3_encode(x: torch.Tensor) -> torch.Tensor:
+    """Nearest e4m3 code, ties to the even code, saturating at +-448 (float64 in)."""
+    x = _f64(x)
+    if torch.isnan(x).any():
+        raise ValueError("NaN has no reading here")
+    a = x.abs().clamp(max=E4M3_MAX)
+    # spacing of the representable values around a: 2^(e-3) for a in [2^e, 2^(e+1)),
+    # e >= -6; below 2^-6 (subnormals) the spacing stays 2^-9
+    e = _binade(a).clamp(min=-6.0)
+    quantum = torch.ldexp(torch.ones_like(a), (e - 3))
+    # torch.round is round-half-to-even on the integer multiple of the quantum
+    q = torch.round(a / quantum) * quantum          # at most 448: a <= 448 and 448 is a code
+    # code of the non-negative value q
+    qe = _binade(q)
+    is_sub = q < 2.0 ** -6
+    mant_sub = torch.round(q / 2.0 ** -9)
+    mant_norm = torch.round((q / torch.ldexp(torch.ones_like(q), qe) - 1.0) * 8.0)
+    code = torch.where(is_sub, mant_sub, (qe + 7) * 8 + mant_norm).to(torch.int64)
+    code = torch.where(torch.signbit(x), code | 128, code)
+    # a negative value that rounds to zero keeps its sign bit (-0, code 0x80)
+    return code.to(torch.uint8)
+
+
+def e4m3_step(codes: torch.Tensor) -> torch.Tensor:
+    """Distance from |decode(code)| to the next larger representable magnitude."""
+    c = codes.to(torch.int64) & 127
+    nxt = (c + 1).clamp(max=126)
+    return e4m3_decode(nxt) - e4m3_decode(c)
+
+
+def e4m3_near_tie(x: torch.Tensor, rel: float = 1e-5, atol=0.0) -> torch.Tensor:
+    """True where |x| lies within max(rel |x|, atol) of a midpoint between two codes.
+
+    There a difference in how x was computed (its rounding error, at most that
+    distance) may flip the code to its neighbour; both neighbours are then
+    correct encodings of x.  atol may be a tensor broadcastable to x.
+    """
+    a = _f64(x).abs().clamp(max=E4M3_MAX)
+    lo = e4m3_decode(e4m3_encode(a))
+    step_up = e4m3_step(e4m3_encode(a))
+    below = e4m3_decode((e4m3_encode(a).to(torch.int64) - 1).clamp(min=0).to(torch.uint8))
+    mid_up = lo + 0.5 * step_up
+    mid_dn = 0.5 * (lo + below)
+    tol = torch.maximum(rel * a.clamp(min=2.0 ** -9), torch.as_tensor(atol, dtype=torch.float64))
+    return ((a - mid_up).abs() <= tol) | (((a - mid_dn).abs() <= tol) & (lo > 0))
+
+
+# ---------------------------------------------------------------- the rotation
+
+def hadamard(d: int) -> torch.Tensor:
+    """Sylvester Hadamard matrix of order d (a power of two), float64, entries +-1."""
+    if d < 1 or d & (d - 1):
+        raise ValueError("d must be a power of two")
+    h = torch.ones(1, 1, dtype=torch.float64)
+    while h.shape[0] < d:
+        h = torch.cat([torch.cat([h, h], 1), torch.cat([h, -h], 1)], 0)
+    return h
+
+
+def rotate(x: torch.Tensor, signs: torch.Tensor) -> torch.Tensor:
+    """x diag(sigma) H_d along the last axis (unnormalised: J = this / sqrt(d))."""
+    x = _f64(x)
+    d = x.shape[-1]
+    return torch.matmul(x * _f64(signs).reshape(d), hadamard(d))
+
+
+def quantize_e4m3(x: torch.Tensor, signs: torch.Tensor | None = None):
+    """Per-(batch, head) power-of-two scale and e4m3 codes of x (rotated if signs given).
+
+    Returns (codes uint8 [B, N, H, d], scales float64 [B, H], scaled float64
+    [B, N, H, d] = the values that were rounded, x / s).
+    """
+    xr = rotate(x, signs) if signs is not None else _f64(x)
+    amax = xr.abs().amax(dim=(1, 3))                              # [B, H]
+    e = torch.ceil(torch.log2(torch.where(amax > 0, amax, torch.ones_like(amax)) / E4M3_MAX))
+    s = torch.where(amax > 0, torch.ldexp(torch.ones_like(amax), e), torch.ones_like(amax))
+    scaled = xr / s[:, None, :, None]
+    return e4m3_encode(scaled), s, scaled
+
+
+# ------------------------------------------------------------- fp8 attention
+
+def fp8_attention_forward(q8, k8, v8, sq, sk, sv, qk_scale: float, causal: bool,
+                          tie_rel: float = 1e-5, q_scaled=None, k_scaled=None, v_scaled=None,
+                          q_tie_atol=0.0, k_tie_atol=0.0, block: int | None = KEY_BLOCK):
+    """Attention over decoded e4m3 codes with the P V product on e4m3 probabilities.
+
+    q8 [B, Nq, H, d], k8/v8 [B, Nk, H, d] uint8 codes; sq, sk, sv [B, H] scales;
+    S = qk_scale * sq * sk * (q8 . k8).  The keys are visited in blocks of
+    ``block`` (None: one block) with the online softmax's running maximum m
+    ("08 · FlashAttention", §二): per block, P~ = exp(S - m_new) <= 1 is rounded
+    as e4m3(256 P~) for the P V product, earlier blocks' sums are rescaled by
+    e^(m - m_new), and the row sum l keeps the unrounded P~.  Rounding P~ at the
+    running maximum rather than the final one is what a one-pass kernel can do;
+    with one block the two agree.
+
+    Returns (O, LSE, slack_o, slack_lse): slack bounds, to first order, how far
+    O and LSE may move when codes that sit at a near-tie (P~, and Q, K, V when
+    their pre-rounding values q_scaled/k_scaled/v_scaled are given) round to the
+    neighbouring code; a code counts as near a tie within max(tie_rel |x|,
+    *_tie_atol) of a midpoint.
+    """
+    qd, kd, vd = e4m3_decode(q8), e4m3_decode(k8), e4m3_decode(v8)
+    B, Nq, H, d = qd.shape
+    Nk = kd.shape[1]
+    if causal and Nq != Nk:
+        raise ValueError("causal attention needs Nq == Nk")
+    sq, sk, sv = _f64(sq), _f64(sk), _f64(sv)
+    o = torch.zeros(B, Nq, H, d, dtype=torch.float64)
+    lse = torch.full((B, H, Nq), _NEG_INF, dtype=torch.float64)
+    slack_o = torch.zeros_like(o)
+    slack_l = torch.zeros_like(lse)
+    if Nk == 0:
+        return o, lse, slack_o, slack_l
+    bs = Nk if block is None else int(block)
+
+    def tie_steps(scaled, codes, atol=0.0):
+        if scaled is None:
+            return torch.zeros(codes.shape, dtype=torch.float64)
+        return e4m3_near_tie(scaled, tie_rel, atol).to(torch.float64) * e4m3_step(codes)
+
+    tq, tk = tie_steps(q_scaled, q8, q_tie_atol), tie_steps(k_scaled, k8, k_tie_atol)
+    tv = tie_steps(v_scaled, v8)
+    for b in range(B):
+        for h in range(H):
+            c = qk_scale * float(sq[b, h]) * float(sk[b, h])
+            svh = float(sv[b, h])
+            qh, kh, vh = qd[b, :, h], kd[b, :, h], vd[b, :, h]
+            s = c * torch.matmul(qh, kh.transpose(0, 1))              # [Nq, Nk]
+            # |dS| from Q/K codes at a near-tie flipping by one step
+            ds = c * (torch.matmul(tq[b, :, h], kh.abs().transpose(0, 1))
+                      + torch.matmul(qh.abs(), tk[b, :, h].transpose(0, 1)))
+            if causal:
+                vis = torch.arange(Nk).unsqueeze(0) <= torch.arange(Nq).unsqueeze(1)
+                s = s.masked_fill(~vis, _NEG_INF)
+                ds = ds.masked_fill(~vis, 0.0)
+            m_fin = s.amax(dim=-1, keepdim=True)
+            live = m_fin > _NEG_INF
+            m_fin0 = torch.where(live, m_fin, torch.zeros_like(m_fin))
+            # the online pass over key blocks
+            m = torch.full((Nq, 1), _NEG_INF, dtype=torch.float64)
+            acc = torch.zeros(Nq, d, dtype=torch.float64)
+            l = torch.zeros(Nq, 1, dtype=torch.float64)
+            tie_p = torch.zeros(Nq, d, dtype=torch.float64)   # P-tie steps * |v|, final units
+            tie_v = torch.zeros(Nq, d, dtype=torch.float64)   # p8 * V-tie steps, final units
+            for j0 in range(0, Nk, bs):
+                sb = s[:, j0:j0 + bs]
+                m_new = torch.maximum(m, sb.amax(dim=-1, keepdim=True))
+                m_ref = torch.where(m_new > _NEG_INF, m_new, torch.zeros_like(m_new))
+                alpha = torch.exp(m - m_ref)
+                pt = torch.exp(sb - m_ref)                            # P~ <= 1 at the running max
+                p8 = e4m3_encode(P_SCALE * pt)
+                pq = e4m3_decode(p8)
+                acc = alpha * acc + torch.matmul(pq, vh[j0:j0 + bs])
+                l = alpha * l + pt.sum(dim=-1, keepdim=True)
+                m = m_new
+                to_fin = torch.exp(m_ref - m_fin0)                   # later rescaling of this block
+                tp = e4m3_near_tie(P_SCALE * pt, tie_rel).to(torch.float64) * e4m3_step(p8)
+                tie_p += to_fin * torch.matmul(tp, vh[j0:j0 + bs].abs())
+                tie_v += to_fin * torch.matmul(pq, tv[b, j0:j0 + bs, h])
+            linv = torch.where(live, 1.0 / l, torch.zeros_like(l))
+            o[b, :, h] = svh / P_SCALE * acc * linv
+            lse[b, h] = torch.where(live, m + torch.log(l), torch.full_like(m, _NEG_INF)).squeeze(-1)
+            # slack: P codes at a near-tie, V codes at a near-tie, and dS (first order)
+            p_true = torch.exp(s - m_fin0) * torch.where(live, 1.0 / torch.exp(s - m_fin0).sum(-1, keepdim=True), torch.zeros_like(l))
+            vabs = vh.abs() * svh
+            so = svh / P_SCALE * (tie_p + tie_v) * linv
+            dev = torch.matmul(p_true * ds, vabs) + (p_true * ds).sum(-1, keepdim=True) * o[b, :, h].abs()
+            slack_o[b, :, h] = so + dev
+            slack_l[b, h] = (p_true * ds).sum(dim=-1)
+    return o, lse, slack_o, slack_l
+
+
+def fp32_rotation_error(x: torch.Tensor, signs: torch.Tensor, s: torch.Tensor) -> torch.Tensor:
+    """Bound on |fp32 rotation - exact| / s per row: a fast Walsh-Hadamard
+    transform in fp32 rounds once per butterfly stage, each rounding at most
+    2^-24 of a partial sum bounded by the row's L1 norm, log2(d) stages.
+    Returns [B, N, H, 1]."""
+    x = _f64(x)
+    d = x.shape[-1]
+    l1 = (x * _f64(signs).reshape(d)).abs().sum(dim=-1, keepdim=True)
+    return math.log2(d) * 2.0 ** -24 * l1 / _f64(s)[:, None, :, None]
+
+
+def fp8_forward(q, k, v, signs, scale: float, causal: bool, rotate_qk: bool = True,
+                tie_rel: float = 1e-5, fp32_rotation: bool = False):
+    """The whole FP8 forward from bf16/float inputs: rotate, quantise, attend.
+
+    With fp32_rotation, codes of Q and K within twice the fp32 rotation's
+    rounding bound of a midpoint count as near a tie (a kernel that rotates in
+    fp32 may round them either way).
+    Returns (O, LSE, slack_o, slack_lse, (q8, k8, v8), (sq, sk, sv)).
+    """
+    d = q.shape[-1]
+    sg = signs if rotate_qk else None
+    q8, sq, qs = quantize_e4m3(q, sg)
+    k8, sk, ks = quantize_e4m3(k, sg)
+    v8, sv, vs = quantize_e4m3(v, None)
+    qk_scale = scale / d if rotate_qk else scale
+    qa = ka = 0.0
+    if fp32_rotation and rotate_qk:
+        qa = 2.0 * fp32_rotation_error(q, signs, sq)
+        ka = 2.0 * fp32_rotation_error(k, signs, sk)
+    o, lse, so, sl = fp8_attention_forward(q8, k8, v8, sq, sk, sv, qk_scale, causal, tie_rel,
+                                           qs, ks, vs, qa, ka)
+    return o, lse, so, sl, (q8, k8, v8), (sq, sk, sv)
+
+
+def rmse(a: torch.Tensor, b: torch.Tensor) -> float:
+    """Root-mean-square difference."""
+    return math.sqrt(float(((_f64(a) - _f64(b)) ** 2).mean()))

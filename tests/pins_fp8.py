@@ -1,0 +1,242 @@
+"""Checks that tie the FP8 oracle (oracle/fp8.py) to facts outside it.
+
+Each ``pin_*`` takes a module with the functions of oracle/fp8.py (normally
+``oracle.fp8``; the mutation tests pass copies with a planted mistake).  The
+facts:
+
+* the OCP E4M3 format: the values of named codes (the format's definition:
+  bias 7, three mantissa bits, 448 the largest finite value, S.1111.111 NaN),
+  and encoding = the nearest code by exhaustive search, ties to the even code;
+* the Sylvester Hadamard matrix is scipy's ``hadamard`` and H H^T = d I, so
+  J = diag(sigma) H / sqrt(d) is orthogonal and (QJ)(KJ)^T = Q K^T ("LLM Systems
+  22: Flash Attention", §4.1.3);
+* with scores whose exponentials are exact powers of two, P~ quantises without
+  loss and the FP8 attention must equal the float64 dense oracle (pinned on its
+  own) on the decoded inputs; in general the difference is bounded by half an
+  e4m3 step of each P~;
+* the whole FP8 forward stays close to exact attention, and the rotation lowers
+  the error when a few channels of Q and K carry outliers (the page's claim).
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import scipy.linalg
+import torch
+
+import oracle as dense
+
+
+def _rand(shape, seed, scale=1.0):
+    g = torch.Generator().manual_seed(seed)
+    return torch.randn(shape, generator=g, dtype=torch.float64) * scale
+
+
+def _signs(d, seed):
+    g = torch.Generator().manual_seed(seed)
+    return torch.randint(0, 2, (d,), generator=g).to(torch.float64) * 2 - 1
+
+
+def pin_e4m3_named_codes(f):
+    known = {0x00: 0.0, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0x08: 2.0 ** -6, 0x38: 1.0,
+             0x39: 1.125, 0x3F: 1.875, 0x40: 2.0, 0x77: 240.0, 0x78: 256.0, 0x7E: 448.0,
+             0x80: -0.0, 0xB8: -1.0, 0xFE: -448.0}
+    codes = torch.tensor(sorted(known), dtype=torch.uint8)
+    vals = f.e4m3_decode(codes)
+    for c, v in zip(codes.tolist(), vals.tolist()):
+        assert v == known[c], (hex(c), v)
+    assert torch.isnan(f.e4m3_decode(torch.tensor([0x7F, 0xFF], dtype=torch.uint8))).all()
+    # magnitudes rise strictly with the code; the sign bit only negates
+    pos = f.e4m3_decode(torch.arange(127, dtype=torch.uint8))
+    assert bool((pos[1:] > pos[:-1]).all())
+    neg = f.e4m3_decode(torch.arange(128, 255, dtype=torch.uint8))
+    assert torch.equal(neg, -pos)
+
+
+def _nearest_bruteforce(f, x):
+    """Encode by search over every finite code; ties -> even code; |x| > 448 -> 448."""
+    codes = torch.arange(127, dtype=torch.uint8)
+    vals = f.e4m3_decode(codes).tolist()
+    out = []
+    for xv in x.tolist():
+        a = min(abs(xv), 448.0)
+        best = min(range(127), key=lambda c: (abs(a - vals[c]), c & 1))
+        out.append(best | (128 if math.copysign(1.0, xv) < 0 else 0))
+    return torch.tensor(out, dtype=torch.uint8)
+
+
+def pin_e4m3_encode_is_nearest(f):
+    rng = np.random.default_rng(401)
+    mags = np.exp(rng.uniform(np.log(1e-4), np.log(600.0), 3000))
+    x = mags * rng.choice([-1.0, 1.0], mags.size)
+    vals = f.e4m3_decode(torch.arange(127, dtype=torch.uint8)).numpy()
+    mids = 0.5 * (vals[1:] + vals[:-1])
+    x = np.concatenate([x, mids, -mids, vals, [449.0, 464.0, 500.0, 1e6, -1e6, 2.0 ** -10, 3 * 2.0 ** -11]])
+    xt = torch.tensor(x, dtype=torch.float64)
+    assert torch.equal(f.e4m3_encode(xt), _nearest_bruteforce(f, xt))
+
+
+def pin_hadamard(f):
+    for d in (1, 2, 4, 8, 16, 32, 64, 128):
+        h = f.hadamard(d)
+        assert torch.equal(h, torch.tensor(scipy.linalg.hadamard(d), dtype=torch.float64))
+        assert torch.equal(h @ h.T, d * torch.eye(d, dtype=torch.float64))
+
+
+def pin_rotation_keeps_scores(f):
+    d = 64
+    q, k = _rand((5, d), 402), _rand((7, d), 403)
+    sg = _signs(d, 404)
+    qr, kr = f.rotate(q, sg), f.rotate(k, sg)
+    ref = d * (q @ k.T)
+    assert (qr @ kr.T - ref).abs().max().item() < 1e-11 * ref.abs().max().item()
+    # the rotation really mixes: a one-hot row spreads over every dimension
+    e0 = torch.zeros(1, d, dtype=torch.float64)
+    e0[0, 3] = 1.0
+    assert bool((f.rotate(e0, sg).abs() == 1.0).all())
+    # J = diag(sigma) H / sqrt(d): unit vector i goes to sigma_i times row i of H,
+    # and row i of the Sylvester matrix is (-1)^popcount(i & j) over j
+    for i in (0, 3, 37, 63):
+        ei = torch.zeros(1, d, dtype=torch.float64)
+        ei[0, i] = 1.0
+        row = torch.tensor([(-1.0) ** bin(i & j).count("1") for j in range(d)], dtype=torch.float64)
+        assert torch.equal(f.rotate(ei, sg)[0], float(sg[i]) * row), i
+
+
+def pin_quantize_scale_and_codes(f):
+    x = _rand((2, 33, 3, 64), 405, 3.0)
+    x[1, :, 2] = 0.0                                    # an all-zero head: scale 1, codes 0
+    sg = _signs(64, 406)
+    for signs in (None, sg):
+        codes, s, scaled = f.quantize_e4m3(x, signs)
+        xr = f.rotate(x, signs) if signs is not None else x
+        amax = xr.abs().amax(dim=(1, 3))
+        for b in range(2):
+            for h in range(3):
+                sv = float(s[b, h])
+                if float(amax[b, h]) == 0.0:
+                    assert sv == 1.0 and int(codes[b, :, h].to(torch.int64).abs().max()) in (0, 128)
+                    continue
+                m, e = math.frexp(sv)
+                assert m == 0.5, sv                     # a power of two
+                r = float(amax[b, h]) / sv
+                assert 224.0 < r <= 448.0, r            # the smallest such power
+        dec = f.e4m3_decode(codes) * s[:, None, :, None]
+        # each code within half a step of its value (relative 2^-4, or 2^-10 absolute in subnormals)
+        err = (dec - xr).abs() / s[:, None, :, None]
+        assert bool((err <= torch.maximum(xr.abs() / s[:, None, :, None] / 16, torch.full_like(err, 2.0 ** -10)) * (1 + 1e-12)).all())
+        assert torch.allclose(scaled * s[:, None, :, None], xr, rtol=0, atol=0)
+
+
+def _exact_case(causal):
+    """Codes for Q, K in {-1, 0, 1} (d = 8) and random representable V, scales 1."""
+    g = torch.Generator().manual_seed(407)
+    B, N, H, d = 2, 19, 2, 8
+    qv = torch.randint(-1, 2, (B, N, H, d), generator=g).to(torch.float64)
+    kv = torch.randint(-1, 2, (B, N, H, d), generator=g).to(torch.float64)
+    vc = torch.randint(0, 127, (B, N, H, d), generator=g) | (torch.randint(0, 2, (B, N, H, d), generator=g) << 7)
+    return qv, kv, vc.to(torch.uint8)
+
+
+def pin_fp8_attention_exact_powers_of_two(f):
+    # qk_scale = ln 2 and integer dot products in [-8, 8]: every P~ is 2^-k with
+    # k <= 16, so 256 P~ is an exact e4m3 value and nothing is lost
+    for causal in (False, True):
+        qv, kv, v8 = _exact_case(causal)
+        q8, k8 = f.e4m3_encode(qv), f.e4m3_encode(kv)
+        ones = torch.ones(2, 2, dtype=torch.float64)
+        for sv in (1.0, 0.25):
+            o, lse, _, _ = f.fp8_attention_forward(q8, k8, v8, ones, ones, ones * sv, math.log(2.0), causal)
+            vd = f.e4m3_decode(v8) * sv
+            o_ref, lse_ref = dense.attention_forward(qv, kv, vd, math.log(2.0), causal)
+            assert (o - o_ref).abs().max().item() < 1e-12, (causal, sv)
+            assert (lse - lse_ref).abs().max().item() < 1e-12, (causal, sv)
+        # the scales multiply the scores
+        o2, lse2, _, _ = f.fp8_attention_forward(q8, k8, v8, ones * 2.0, ones * 0.5, ones, math.log(2.0), causal)
+        assert (o2 - f.fp8_attention_forward(q8, k8, v8, ones, ones, ones, math.log(2.0), causal)[0]).abs().max().item() < 1e-12
+        o4, _, _, _ = f.fp8_attention_forward(q8, k8, v8, ones * 2.0, ones, ones, math.log(2.0) / 2, causal)
+        assert (o4 - o2).abs().max().item() < 1e-12
+
+
+def pin_fp8_running_max_worked_example(f):
+    # one query (q = e_0), three keys with k_0 = 2, 1, 3 and scores c k, c = ln 3,
+    # values v_0 = 1, 3, 4; keys in blocks of 2.  Block {0, 1}: running max at key 0,
+    # P~ = 1, 1/3 -> e4m3(256) = 256, e4m3(85.33) = 88.  Block {2}: max rises by
+    # ln 3, earlier terms scale by 1/3, P~ = 1 -> 256.  l = 1/3 + 1/9 + 1 = 13/9.
+    # O_0 = ((256 * 1 + 88 * 3) / 3 + 256 * 4) / (256 * 13 / 9); LSE = 3 ln 3 + ln(13/9).
+    # (Rounded at the final maximum instead: 88, 28, 256 -> a different O_0.)
+    enc = f.e4m3_encode
+    d = 4
+    q8 = enc(torch.tensor([[[[1.0, 0, 0, 0]]]], dtype=torch.float64))
+    k8 = enc(torch.tensor([[[[2.0, 0, 0, 0]], [[1.0, 0, 0, 0]], [[3.0, 0, 0, 0]]]], dtype=torch.float64))
+    v8 = enc(torch.tensor([[[[1.0, 0, 0, 0]], [[3.0, 0, 0, 0]], [[4.0, 0, 0, 0]]]], dtype=torch.float64))
+    one = torch.ones(1, 1, dtype=torch.float64)
+    o, lse, _, _ = f.fp8_attention_forward(q8, k8, v8, one, one, one, math.log(3.0), False, block=2)
+    want = ((256 * 1 + 88 * 3) / 3 + 256 * 4) / (256 * 13 / 9)
+    assert abs(o[0, 0, 0, 0].item() - want) < 1e-12, (o[0, 0, 0, 0].item(), want)
+    assert abs(lse[0, 0, 0].item() - (3 * math.log(3.0) + math.log(13 / 9))) < 1e-12
+    # one block: rounded at the final maximum
+    o1, _, _, _ = f.fp8_attention_forward(q8, k8, v8, one, one, one, math.log(3.0), False, block=None)
+    assert abs(o1[0, 0, 0, 0].item() - (88 * 1 + 28 * 3 + 256 * 4) / (256 * 13 / 9)) < 1e-12
+    assert d == q8.shape[-1]
+
+
+def pin_fp8_attention_p_rounding_bound(f):
+    # random codes: the only difference from exact attention on the decoded inputs
+    # is rounding 256 P~ to e4m3: |dP~| <= max(P~ / 16, 2^-10 / 256)
+    g = torch.Generator().manual_seed(408)
+    B, N, H, d = 1, 40, 2, 16
+    q8 = torch.randint(0, 255, (B, N, H, d), generator=g).to(torch.uint8)
+    k8 = torch.randint(0, 255, (B, N, H, d), generator=g).to(torch.uint8)
+    v8 = torch.randint(0, 255, (B, N, H, d), generator=g).to(torch.uint8)
+    for t in (q8, k8, v8):
+        t[(t & 127) == 127] = 0x38                     # no NaN codes
+    sq = torch.full((B, H), 2.0 ** -6, dtype=torch.float64)
+    sk = torch.full((B, H), 2.0 ** -5, dtype=torch.float64)
+    sv = torch.full((B, H), 2.0 ** -3, dtype=torch.float64)
+    for causal in (False, True):
+        o, lse, _, _ = f.fp8_attention_forward(q8, k8, v8, sq, sk, sv, 0.37, causal)
+        qd = f.e4m3_decode(q8) * sq[0, 0]
+        kd = f.e4m3_decode(k8) * sk[0, 0]
+        vd = f.e4m3_decode(v8) * sv[0, 0]
+        o_ref, lse_ref = dense.attention_forward(qd, kd, vd, 0.37, causal)
+        p = dense.attention_probs(qd, kd, 0.37, causal)            # [B, H, N, N]
+        bound = torch.einsum("bhij,bjhd->bihd", p / 16 + 2.0 ** -18, vd.abs())
+        diff = (o - o_ref).abs()
+        assert bool((diff <= bound * (1 + 1e-9) + 1e-13).all()), causal
+        assert diff.max().item() > 1e-6                            # P~ is rounded
+        assert (lse - lse_ref).abs().max().item() < 1e-10
+
+
+def pin_fp8_forward_close_and_rotation_helps(f):
+    B, N, H, d = 1, 96, 2, 64
+    q, k, v = _rand((B, N, H, d), 409), _rand((B, N, H, d), 410), _rand((B, N, H, d), 411)
+    sg = _signs(d, 412)
+    scale = d ** -0.5
+    o_ref, lse_ref = dense.attention_forward(q, k, v, scale, False)
+    o_rot = f.fp8_forward(q, k, v, sg, scale, False, rotate_qk=True)[0]
+    assert f.rmse(o_rot, o_ref) < 3e-2
+    # outliers: two channels of Q and K twenty times larger
+    qo, ko = q.clone(), k.clone()
+    qo[..., [5, 40]] *= 20.0
+    ko[..., [5, 40]] *= 20.0
+    scale_o = 0.02
+    o_ref2, _ = dense.attention_forward(qo, ko, v, scale_o, False)
+    e_plain = f.rmse(f.fp8_forward(qo, ko, v, sg, scale_o, False, rotate_qk=False)[0], o_ref2)
+    e_rot = f.rmse(f.fp8_forward(qo, ko, v, sg, scale_o, False, rotate_qk=True)[0], o_ref2)
+    assert e_rot < e_plain, (e_rot, e_plain)
+
+
+ALL_PINS = [
+    pin_e4m3_named_codes,
+    pin_e4m3_encode_is_nearest,
+    pin_hadamard,
+    pin_rotation_keeps_scores,
+    pin_quantize_scale_and_codes,
+    pin_fp8_attention_exact_powers_of_two,
+    pin_fp8_running_max_worked_example,
+    pin_fp8_attention_p_rounding_bound,
+    pin_fp8_forward_close_and_rotation_helps,
+]

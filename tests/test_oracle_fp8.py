@@ -1,0 +1,89 @@
+"""The FP8 oracle against its pins, and planted mistakes against the pins (CPU)."""
+
+import os
+import types
+
+import pytest
+
+import oracle.fp8 as fp8
+from tests import pins_fp8
+
+SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                   "oracle", "fp8.py")
+
+MUTATIONS = {
+    "decode_bias_8": ("normal = torch.ldexp(1.0 + m / 8.0, (e - 7).to(torch.float64))",
+                      "normal = torch.ldexp(1.0 + m / 8.0, (e - 8).to(torch.float64))"),
+    "decode_subnormal_exponent": ("sub = torch.ldexp(m / 8.0, torch.full_like(m, -6.0))",
+                                  "sub = torch.ldexp(m / 8.0, torch.full_like(m, -7.0))"),
+    "encode_ties_away": ("q = torch.round(a / quantum) * quantum",
+                         "q = torch.floor(a / quantum + 0.5) * quantum"),
+    "encode_truncates": ("q = torch.round(a / quantum) * quantum",
+                         "q = torch.floor(a / quantum) * quantum"),
+    "encode_no_saturation": ("a = x.abs().clamp(max=E4M3_MAX)\n    # spacing",
+                             "a = x.abs()\n    # spacing"),
+    "encode_subnormal_spacing": ("e = _binade(a).clamp(min=-6.0)", "e = _binade(a).clamp(min=-7.0)"),
+    "encode_drops_sign": ("code = torch.where(torch.signbit(x), code | 128, code)", "code = code"),
+    "hadamard_not_orthogonal": ("h = torch.cat([torch.cat([h, h], 1), torch.cat([h, -h], 1)], 0)",
+                                "h = torch.cat([torch.cat([h, h], 1), torch.cat([-h, h], 1)], 0)"),
+    "rotate_ignores_signs": ("return torch.matmul(x * _f64(signs).reshape(d), hadamard(d))",
+                             "return torch.matmul(x, hadamard(d))"),
+    "rotate_transposed_signs": ("return torch.matmul(x * _f64(signs).reshape(d), hadamard(d))",
+                                "return torch.matmul(x, hadamard(d)) * _f64(signs).reshape(d)"),
+    "scale_not_power_of_two": ("s = torch.where(amax > 0, torch.ldexp(torch.ones_like(amax), e), torch.ones_like(amax))",
+                               "s = torch.where(amax > 0, amax / E4M3_MAX, torch.ones_like(amax))"),
+    "scale_rounds_down": ("e = torch.ceil(torch.log2(", "e = torch.floor(torch.log2("),
+    "scores_missing_k_scale": ("c = qk_scale * float(sq[b, h]) * float(sk[b, h])",
+                               "c = qk_scale * float(sq[b, h])"),
+    "p_scale_not_undone": ("o[b, :, h] = svh / P_SCALE * acc * linv", "o[b, :, h] = svh * acc * linv"),
+    "v_scale_dropped": ("o[b, :, h] = svh / P_SCALE * acc * linv", "o[b, :, h] = 1.0 / P_SCALE * acc * linv"),
+    "p_not_quantised": ("p8 = e4m3_encode(P_SCALE * pt)\n                pq = e4m3_decode(p8)",
+                        "p8 = e4m3_encode(P_SCALE * pt)\n                pq = P_SCALE * pt"),
+    "p_rounded_at_final_max": ("p8 = e4m3_encode(P_SCALE * pt)\n                pq = e4m3_decode(p8)",
+                               "p8 = e4m3_encode(P_SCALE * torch.exp(sb - m_fin0))\n"
+                               "                pq = e4m3_decode(p8) * torch.exp(m_fin0 - m_ref)"),
+    "acc_not_rescaled": ("acc = alpha * acc + torch.matmul(pq, vh[j0:j0 + bs])",
+                         "acc = acc + torch.matmul(pq, vh[j0:j0 + bs])"),
+    "sum_not_rescaled": ("l = alpha * l + pt.sum(dim=-1, keepdim=True)",
+                         "l = l + pt.sum(dim=-1, keepdim=True)"),
+    "block_offset_ignored": ("acc = alpha * acc + torch.matmul(pq, vh[j0:j0 + bs])",
+                             "acc = alpha * acc + torch.matmul(pq, vh[0:sb.shape[1]])"),
+    "causal_off_by_one": ("vis = torch.arange(Nk).unsqueeze(0) <= torch.arange(Nq).unsqueeze(1)",
+                          "vis = torch.arange(Nk).unsqueeze(0) < torch.arange(Nq).unsqueeze(1)"),
+    "lse_missing_max": ("lse[b, h] = torch.where(live, m + torch.log(l),",
+                        "lse[b, h] = torch.where(live, torch.log(l),"),
+    "rotation_norm_missing": ("qk_scale = scale / d if rotate_qk else scale",
+                              "qk_scale = scale"),
+    "v_rotated_too": ("v8, sv, vs = quantize_e4m3(v, None)", "v8, sv, vs = quantize_e4m3(v, sg)"),
+}
+
+
+@pytest.mark.parametrize("pin", pins_fp8.ALL_PINS, ids=lambda f: f.__name__)
+def test_pin(pin):
+    pin(fp8)
+
+
+def _mutant(find, repl):
+    src = open(SRC).read()
+    assert src.count(find) == 1, f"mutation anchor must occur once: {find!r}"
+    mod = types.ModuleType("fp8_mutant")
+    exec(compile(src.replace(find, repl), "fp8_mutant", "exec"), mod.__dict__)
+    return mod
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_pins_catch_mutation(name):
+    mod = _mutant(*MUTATIONS[name])
+    caught = []
+    for pin in pins_fp8.ALL_PINS:
+        try:
+            pin(mod)
+        except Exception as e:  # AssertionError, or the mutant crashing outright
+            caught.append((pin.__name__, type(e).__name__))
+    assert caught, f"no pin noticed mutation {name}"
+
+
+def test_unmutated_copy_passes():
+    mod = _mutant('_NEG_INF = float("-inf")', '_NEG_INF = float("-inf")')
+    for pin in pins_fp8.ALL_PINS:
+        pin(mod)
