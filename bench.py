@@ -245,6 +245,123 @@ def run_decode(args, w):
     print(json.dumps(out), flush=True)
 
 
+FP8_METRIC = "FP8 (e4m3, Hadamard-rotated Q/K) attention forward TFLOP/s, % fp8 MFMA peak, B8 H16 N4096 d128 causal"
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
+
+
+def fp8_cpu_baseline(x, base, budget_s: float):
+    """Time the fp64 FP8 oracle (rotate, quantise, attend) one (batch, head) at a time."""
+    import oracle.fp8 as of8   # test infrastructure: only this leg of the benchmark uses it
+
+    torch.set_num_threads(len(os.sched_getaffinity(0)))
+    B, N, H, d = x["q"].shape
+    done, t_total = 0, 0.0
+    for b in range(B):
+        for h in range(H):
+            sl = slice(h, h + 1)
+            t0 = time.perf_counter()
+            of8.fp8_forward(x["q"][b:b + 1, :, sl], x["k"][b:b + 1, :, sl], x["v"][b:b + 1, :, sl],
+                            x["signs"], base.scale, True)
+            t_total += time.perf_counter() - t0
+            done += 1
+            if t_total >= budget_s:
+                break
+        if t_total >= budget_s:
+            break
+    flops = acc.flops_fwd(acc.pairs(N, N, True), d) * done
+    return {"value": round(flops / t_total / 1e12, 6), "unit": "TFLOP/s",
+            "cores": torch.get_num_threads(), "kind": "oracle",
+            "sample": f"{done} of {B * H} (batch, head) slices, FP8 forward (rotation, quantisation, "
+                      f"blocked attention, tie bounds), float64, {t_total:.1f} s",
+            "cpu": cpu_model()}
+
+
+def run_fp8(args, w8):
+    """FP8 forward: one step = fa_fwd_fp8 (block maxima, quantisation, attention kernels)."""
+    base = wl.WORKLOADS[w8.base]
+    dev = torch.device("cuda", 0)
+    x = wl.make_inputs(w8.name)
+    q, k, v, sg = (x[n].to(dev) for n in ("q", "k", "v", "signs"))
+    B, N, H, d = q.shape
+    o = torch.empty_like(q)
+    lse = torch.empty(B, H, N, dtype=torch.float32, device=dev)
+    nbytes = fa355.fa_fp8_workspace_bytes(B, N, N, H, d)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    step = lambda: fa355.fa_fwd_fp8(q, k, v, sg, o, lse, ws, base.scale, True, True)
+    calibration_copy(dev)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    q8, k8, v8, sc = fa355.fp8_workspace_views(ws, B, N, N, H, d)
+    sq, sk, sv = (sc[i].reshape(-1) for i in range(3))
+    o2 = torch.empty_like(o)
+    lse2 = torch.empty_like(lse)
+    attn = lambda: fa355.fa_fwd_fp8_codes(q8, k8, v8, sq, sk, sv, o2, lse2, base.scale / d, True)
+
+    def timed(fn):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        ev[0].record()
+        for i in range(args.steps):
+            fn()
+            ev[i + 1].record()
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) / args.steps
+        ts = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps))
+        return wall, ts
+
+    wall, ts_step = timed(step)
+    for _ in range(2):
+        attn()
+    _, ts_attn = timed(attn)
+    flops = acc.flops_fwd(acc.pairs(N, N, True), d) * B * H
+    ms_step = sum(ts_step) / len(ts_step)
+    ms_attn = sum(ts_attn) / len(ts_attn)
+    rate = flops / (ms_attn * 1e-3) / 1e12
+    # compulsory bytes of the attention kernel: codes of q, k, v in, o (bf16) and lse out
+    attn_bytes = 3 * B * N * H * d + B * N * H * d * 2 + B * H * N * 4
+    # quantisation: q, k, v read twice (block maxima, then codes), codes written
+    quant_bytes = 2 * 3 * B * N * H * d * 2 + 3 * B * N * H * d
+    traffic = measured_traffic(w8.name)
+    out = {
+        "metric": FP8_METRIC,
+        "value": round(flops / wall / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3",
+        "data": "synthetic",
+        "config": {"workload": w8.name, "B": B, "H": H, "N": N, "d": d, "causal": True,
+                   "scale": base.scale, "rotation": "random-sign Hadamard"},
+        "step": {"ms": round(ms_step, 4), "ms_median": round(ts_step[len(ts_step) // 2], 4),
+                 "ms_min": round(ts_step[0], 4), "tflops": round(flops / (ms_step * 1e-3) / 1e12, 2)},
+        "kernels": {
+            "fa_fwd_fp8_kernel": {"ms": round(ms_attn, 4), "ms_median": round(ts_attn[len(ts_attn) // 2], 4),
+                                  "ms_min": round(ts_attn[0], 4), "tflops": round(rate, 2),
+                                  "algorithmic_bytes": attn_bytes,
+                                  "traffic": traffic.get("fa_fwd_fp8_kernel") if traffic else None},
+            "fp8_amax_kernel + fp8_quant_kernel": {
+                "ms": round(ms_step - ms_attn, 4),
+                "gbs": round(quant_bytes / max((ms_step - ms_attn) * 1e-3, 1e-9) / 1e9, 1),
+                "algorithmic_bytes": quant_bytes},
+        },
+        "roofline": {"kernel": "fa_fwd_fp8_kernel", "bound": "mfma", "achieved": round(rate, 2),
+                     "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(rate / PEAK_FP8_TFLOPS, 4),
+                     "traffic": traffic.get("fa_fwd_fp8_kernel") if traffic else None,
+                     "algorithmic_bytes": attn_bytes},
+        "device": torch.cuda.get_device_name(0),
+    }
+    out["cpu_baseline"] = fp8_cpu_baseline(x, base, args.cpu_seconds) if args.cpu_seconds > 0 else None
+    print(json.dumps(out), flush=True)
+
+
 def run_varlen(args, w):
     """Packed variable-length workload: one step = fa_fwd_varlen + fa_bwd_varlen."""
     dev = torch.device("cuda", 0)
@@ -324,6 +441,8 @@ def main():
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
+    if args.workload in wl.FP8_WORKLOADS:
+        return run_fp8(args, wl.FP8_WORKLOADS[args.workload])
     if args.workload in wl.DECODE_WORKLOADS:
         return run_decode(args, wl.DECODE_WORKLOADS[args.workload])
     w = wl.WORKLOADS[args.workload]

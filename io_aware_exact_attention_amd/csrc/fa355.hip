@@ -17,6 +17,7 @@
 #include "../../include/fa355.h"
 #include "fa_bwd.hpp"
 #include "fa_decode.hpp"
+#include "fa_fp8.hpp"
 #include "fa_fwd.hpp"
 
 using namespace fa355;
@@ -451,6 +452,143 @@ int fa_fwd_decode(const void* q, const void* k, const void* v, void* o, float* l
     if (hipLaunchKernel(k1, dim3((unsigned)grid1), dim3(64), args, 0, s) != hipSuccess) return FA_ERR_LAUNCH;
     if (hipLaunchKernel(k2, dim3((unsigned)grid2), dim3(d), args, 0, s) != hipSuccess) return FA_ERR_LAUNCH;
     return FA_OK;
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------- FP8 forward
+
+namespace {
+
+size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct Fp8Layout {
+    size_t q8, k8, v8, scales, amax, total;
+    int nblk;
+};
+
+Fp8Layout fp8_layout(int B, int Nq, int Nk, int H) {
+    Fp8Layout L;
+    const size_t bh = (size_t)B * H;
+    L.nblk = (std::max(Nq, Nk) + kFp8QuantRows - 1) / kFp8QuantRows;
+    L.q8 = 0;
+    L.k8 = L.q8 + round256(bh * Nq * kFp8D);
+    L.v8 = L.k8 + round256(bh * Nk * kFp8D);
+    L.scales = L.v8 + round256(bh * Nk * kFp8D);
+    L.amax = L.scales + round256(3 * bh * sizeof(float));
+    L.total = L.amax + round256(3 * bh * L.nblk * sizeof(float));
+    return L;
+}
+
+int check_fp8_shape(int B, int Nq, int Nk, int H, int d, float scale, int causal) {
+    if (B <= 0 || Nq <= 0 || Nk <= 0 || H <= 0) return FA_ERR_SHAPE;
+    if (d != kFp8D) return FA_ERR_UNSUPPORTED;
+    if (!(std::isfinite(scale) && scale > 0.f)) return FA_ERR_UNSUPPORTED;
+    if (causal != 0 && causal != 1) return FA_ERR_UNSUPPORTED;
+    if (causal && Nq != Nk) return FA_ERR_UNSUPPORTED;
+    // one sequence's K/V code rows go through a buffer resource (< 2 GiB)
+    if ((int64_t)Nk * H * d >= ((int64_t)1 << 31)) return FA_ERR_UNSUPPORTED;
+    const int64_t lim = (int64_t)1 << 40;
+    if ((int64_t)B * Nq * H * d > lim || (int64_t)B * Nk * H * d > lim) return FA_ERR_SHAPE;
+    const int64_t n_tiles = (Nq + Fp8Cfg::BM - 1) / Fp8Cfg::BM;
+    if (n_tiles * B * H > INT_MAX) return FA_ERR_SHAPE;
+    const int64_t nblk = (std::max(Nq, Nk) + kFp8QuantRows - 1) / kFp8QuantRows;
+    if (nblk * B * H > INT_MAX) return FA_ERR_SHAPE;
+    return FA_OK;
+}
+
+int launch_fp8_attn(const void* q8, const void* k8, const void* v8, const float* sq, const float* sk,
+                    const float* sv, void* o, float* lse, int B, int Nq, int Nk, int H,
+                    float qk_scale, int causal, hipStream_t s) {
+    Fp8AttnParams p;
+    std::memset(&p, 0, sizeof(p));
+    p.q8 = static_cast<const uint8_t*>(q8);
+    p.k8 = static_cast<const uint8_t*>(k8);
+    p.v8 = static_cast<const uint8_t*>(v8);
+    p.sq = sq;
+    p.sk = sk;
+    p.sv = sv;
+    p.o = static_cast<bf16*>(o);
+    p.lse = lse;
+    p.batch = B;
+    p.H = H;
+    p.nq = Nq;
+    p.nk = Nk;
+    p.n_tiles = (Nq + Fp8Cfg::BM - 1) / Fp8Cfg::BM;
+    p.qk_scale_log2 = qk_scale * kLog2e;
+    const int grid = p.n_tiles * H * B;
+    void* args[] = {&p};
+    const void* k = causal ? reinterpret_cast<const void*>(fa_fwd_fp8_kernel<true>)
+                           : reinterpret_cast<const void*>(fa_fwd_fp8_kernel<false>);
+    return hipLaunchKernel(k, dim3((unsigned)grid), dim3(Fp8Cfg::NW * 64), args, 0, s) == hipSuccess
+               ? FA_OK
+               : FA_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t fa_fp8_workspace_bytes(int B, int Nq, int Nk, int H, int d) {
+    if (B <= 0 || Nq <= 0 || Nk <= 0 || H <= 0 || d != kFp8D) return 0;
+    return fp8_layout(B, Nq, Nk, H).total;
+}
+
+int fa_fwd_fp8(const void* q, const void* k, const void* v, const float* signs, void* o, float* lse,
+               void* workspace, size_t workspace_bytes, int B, int Nq, int Nk, int H, int d,
+               float scale, int causal, int rotate, void* stream) {
+    if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+    if (rotate != 0 && rotate != 1) return FA_ERR_UNSUPPORTED;
+    if (rotate && !signs) return FA_ERR_NULL;
+    int st = check_fp8_shape(B, Nq, Nk, H, d, scale, causal);
+    if (st) return st;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4) ||
+        (rotate && !aligned(signs, 4)) || !aligned(workspace, 256))
+        return FA_ERR_ALIGN;
+    const Fp8Layout L = fp8_layout(B, Nq, Nk, H);
+    if (!workspace || workspace_bytes < L.total) return FA_ERR_WORKSPACE;
+    char* ws = static_cast<char*>(workspace);
+    Fp8QuantParams qp;
+    std::memset(&qp, 0, sizeof(qp));
+    qp.x[0] = static_cast<const bf16*>(q);
+    qp.x[1] = static_cast<const bf16*>(k);
+    qp.x[2] = static_cast<const bf16*>(v);
+    qp.codes[0] = reinterpret_cast<uint8_t*>(ws + L.q8);
+    qp.codes[1] = reinterpret_cast<uint8_t*>(ws + L.k8);
+    qp.codes[2] = reinterpret_cast<uint8_t*>(ws + L.v8);
+    qp.scales = reinterpret_cast<float*>(ws + L.scales);
+    qp.amax = reinterpret_cast<float*>(ws + L.amax);
+    qp.signs = signs;
+    qp.n[0] = Nq;
+    qp.n[1] = Nk;
+    qp.n[2] = Nk;
+    qp.B = B;
+    qp.H = H;
+    qp.nblk = L.nblk;
+    qp.rotate = rotate;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    void* args[] = {&qp};
+    const dim3 qgrid((unsigned)(B * H * L.nblk), 3);
+    if (hipLaunchKernel(reinterpret_cast<const void*>(fp8_amax_kernel), qgrid, dim3(256), args, 0, s) != hipSuccess ||
+        hipLaunchKernel(reinterpret_cast<const void*>(fp8_quant_kernel), qgrid, dim3(256), args, 0, s) != hipSuccess)
+        return FA_ERR_LAUNCH;
+    const size_t bh = (size_t)B * H;
+    const float qk_scale = rotate ? scale / (float)d : scale;
+    return launch_fp8_attn(qp.codes[0], qp.codes[1], qp.codes[2], qp.scales, qp.scales + bh,
+                           qp.scales + 2 * bh, o, lse, B, Nq, Nk, H, qk_scale, causal, s);
+}
+
+int fa_fwd_fp8_codes(const void* q8, const void* k8, const void* v8, const float* sq, const float* sk,
+                     const float* sv, void* o, float* lse, int B, int Nq, int Nk, int H, int d,
+                     float qk_scale, int causal, void* stream) {
+    if (!q8 || !k8 || !v8 || !sq || !sk || !sv || !o || !lse) return FA_ERR_NULL;
+    int st = check_fp8_shape(B, Nq, Nk, H, d, qk_scale, causal);
+    if (st) return st;
+    if (!aligned(q8, 16) || !aligned(k8, 16) || !aligned(v8, 16) || !aligned(o, 16) || !aligned(lse, 4) ||
+        !aligned(sq, 4) || !aligned(sk, 4) || !aligned(sv, 4))
+        return FA_ERR_ALIGN;
+    return launch_fp8_attn(q8, k8, v8, sq, sk, sv, o, lse, B, Nq, Nk, H, qk_scale, causal,
+                           static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

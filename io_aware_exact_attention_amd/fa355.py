@@ -38,6 +38,9 @@ _SIGNATURES = {
     "fa_bwd_dq": (_c_int, [_vp] * 5 + [_sz] + [_vp] + [_c_int] * 5 + [_c_float, _c_int, _vp]),
     "fa_decode_workspace_bytes": (_sz, [_c_int] * 6),
     "fa_fwd_decode": (_c_int, [_vp] * 6 + [_sz] + [_c_int] * 6 + [_c_float, _c_int, _vp]),
+    "fa_fp8_workspace_bytes": (_sz, [_c_int] * 5),
+    "fa_fwd_fp8": (_c_int, [_vp] * 7 + [_sz] + [_c_int] * 5 + [_c_float, _c_int, _c_int, _vp]),
+    "fa_fwd_fp8_codes": (_c_int, [_vp] * 8 + [_c_int] * 5 + [_c_float, _c_int, _vp]),
 }
 
 STATUS = {0: "FA_OK", -1: "FA_ERR_NULL", -2: "FA_ERR_SHAPE", -3: "FA_ERR_UNSUPPORTED",
@@ -175,6 +178,49 @@ def fa_fwd_decode(q, k, v, o, lse, workspace, scale: float, causal: bool, stream
                                _stream(stream)))
 
 
+def fa_fp8_workspace_bytes(B: int, Nq: int, Nk: int, H: int, d: int) -> int:
+    return int(lib().fa_fp8_workspace_bytes(B, Nq, Nk, H, d))
+
+
+def fa_fwd_fp8(q, k, v, signs, o, lse, workspace, scale: float, causal: bool, rotate: bool = True,
+               stream=None):
+    """q [B,Nq,H,d]; k, v [B,Nk,H,d] bf16; signs fp32 [d]; o like q; lse [B,H,Nq] fp32."""
+    B, H, Nq, Nk, d = _dense_dims(q, k)
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(lib().fa_fwd_fp8(_ptr(q), _ptr(k), _ptr(v), _ptr(signs),
+                            _ptr(o), _ptr(lse), _ptr(workspace), nbytes, B, Nq, Nk, H, d,
+                            float(scale), int(bool(causal)), int(bool(rotate)), _stream(stream)))
+
+
+def fa_fwd_fp8_codes(q8, k8, v8, sq, sk, sv, o, lse, qk_scale: float, causal: bool, stream=None):
+    """q8 [B,Nq,H,d], k8, v8 [B,Nk,H,d] uint8 e4m3 codes; sq, sk, sv [B*H] fp32."""
+    B, Nq, H, d = q8.shape
+    Nk = k8.shape[1]
+    _check(lib().fa_fwd_fp8_codes(_ptr(q8), _ptr(k8), _ptr(v8), _ptr(sq), _ptr(sk), _ptr(sv),
+                                  _ptr(o), _ptr(lse), B, Nq, Nk, H, d, float(qk_scale),
+                                  int(bool(causal)), _stream(stream)))
+
+
+def fp8_workspace_views(workspace, B: int, Nq: int, Nk: int, H: int, d: int):
+    """The codes and scales fa_fwd_fp8 leaves in its workspace (views, no copies).
+
+    Offsets follow the documented layout: q8, k8, v8, then scales [3, B*H], each
+    start rounded up to 256 bytes.
+    """
+    def up(x):
+        return (x + 255) // 256 * 256
+    w = workspace.view(torch.uint8)
+    bh = B * H
+    o_k = up(bh * Nq * d)
+    o_v = o_k + up(bh * Nk * d)
+    o_s = o_v + up(bh * Nk * d)
+    q8 = w[:bh * Nq * d].view(B, Nq, H, d)
+    k8 = w[o_k:o_k + bh * Nk * d].view(B, Nk, H, d)
+    v8 = w[o_v:o_v + bh * Nk * d].view(B, Nk, H, d)
+    scales = w[o_s:o_s + 12 * bh].view(torch.float32).view(3, B, H)
+    return q8, k8, v8, scales
+
+
 # ---------------------------------------------------------------------------
 # conveniences: allocate outputs (device memory via torch), then call the ABI
 
@@ -227,4 +273,16 @@ def attention_decode(q, k, v, scale: float, causal: bool, workspace=None):
         nbytes = fa_decode_workspace_bytes(B, Hq, Hkv, Nq, Nk, d)
         workspace = torch.empty(max(nbytes, 16) // 4, dtype=torch.float32, device=q.device)
     fa_fwd_decode(q, k, v, o, lse, workspace, scale, causal)
+    return o, lse
+
+
+def attention_forward_fp8(q, k, v, signs, scale: float, causal: bool, rotate: bool = True,
+                          workspace=None):
+    B, H, Nq, Nk, d = _dense_dims(q, k)
+    o = torch.empty_like(q)
+    lse = torch.empty(B, H, Nq, dtype=torch.float32, device=q.device)
+    if workspace is None:
+        nbytes = fa_fp8_workspace_bytes(B, Nq, Nk, H, d)
+        workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=q.device)
+    fa_fwd_fp8(q, k, v, signs, o, lse, workspace, scale, causal, rotate)
     return o, lse

@@ -11,7 +11,10 @@ Recipe (identical for every consumer):
     ``k_scale`` in fp32 before that single rounding, for peaky rows);
   * packed batches: sequence lengths drawn first, from numpy's
     ``default_rng(seed)``, uniform integers in [min_len, max_len] inclusive;
-  * decoding workloads draw q, k, v only (k and v have the key/value heads).
+  * decoding workloads draw q, k, v only (k and v have the key/value heads);
+  * the FP8 path's random signs (the diagonal of its Hadamard rotation) come
+    from their own generator seeded with ``signs_seed``: integers in {0, 1}
+    mapped to -1, +1, as fp32.
 
 Dense tensors are [B, N, H, d]; packed tensors are [total, H, d].
 """
@@ -102,6 +105,31 @@ DECODE_WORKLOADS = {
 }
 
 
+@dataclasses.dataclass(frozen=True)
+class Fp8Workload:
+    """The FP8 forward on a dense workload's inputs, with the rotation's signs."""
+    name: str
+    base: str            # the dense workload whose q, k, v are used
+    signs_seed: int
+    note: str = ""
+
+
+FP8_WORKLOADS = {
+    w.name: w
+    for w in (
+        Fp8Workload("fp8_b8_h16_n4096_d128_causal", base="b8_h16_n4096_d128_causal", signs_seed=1007,
+                    note="FP8 forward on the B8 H16 N4096 d128 causal inputs"),
+    )
+}
+
+
+def make_signs(d: int, seed: int) -> torch.Tensor:
+    """fp32 [d] of +1 / -1 from a generator of its own."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed))
+    return torch.randint(0, 2, (d,), generator=g).to(torch.float32) * 2 - 1
+
+
 def seq_lengths(nseq: int, min_len: int, max_len: int, seed: int) -> list[int]:
     """Sequence lengths, uniform integers in [min_len, max_len] inclusive."""
     rng = np.random.default_rng(seed)
@@ -168,6 +196,11 @@ def make_decode(B: int, Nq: int, Nk: int, Hq: int, Hkv: int, d: int, seed: int) 
 
 def make_inputs(name: str, with_dout: bool = True) -> dict:
     """Inputs of a named workload (CPU, bf16)."""
+    if name in FP8_WORKLOADS:
+        w8 = FP8_WORKLOADS[name]
+        out = make_inputs(w8.base, with_dout=False)
+        out["signs"] = make_signs(out["q"].shape[-1], w8.signs_seed)
+        return out
     if name in DECODE_WORKLOADS:
         w = DECODE_WORKLOADS[name]
         return make_decode(w.B, w.Nq, w.Nk, w.Hq, w.Hkv, w.d, w.seed)

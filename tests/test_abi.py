@@ -138,6 +138,41 @@ def test_decode_workspace_bytes():
     assert fa355.fa_decode_workspace_bytes(0, 32, 4, 4, 100, 128) == 0
 
 
+def test_fp8_rejects():
+    lib = fa355.lib()
+    W = 1 << 30
+
+    def f8(q=A, k=A, v=A, sg=A, o=A, lse=A, ws=A, wsb=W, B=1, Nq=64, Nk=64, H=2, d=128,
+           scale=0.1, causal=1, rotate=1):
+        return lib.fa_fwd_fp8(q, k, v, sg, o, lse, ws, wsb, B, Nq, Nk, H, d, scale, causal, rotate, None)
+
+    assert f8(q=None) == -1 and f8(lse=None) == -1
+    assert f8(sg=None) == -1                            # rotation needs the signs
+    assert f8(sg=None, rotate=0, ws=None) == -6         # ... unless there is none
+    assert f8(B=0) == -2 and f8(Nq=0) == -2 and f8(H=0) == -2
+    assert f8(d=64) == -3 and f8(scale=float("nan")) == -3 and f8(rotate=2) == -3
+    assert f8(Nq=32, Nk=64, causal=1) == -3
+    assert f8(ws=None) == -6 and f8(wsb=16) == -6
+    assert f8(k=MIS) == -4 and f8(ws=A + 16) == -4 and f8(sg=A + 2) == -4
+    assert f8(H=64, Nk=1 << 18) == -3                   # one sequence's code rows span 2 GiB
+
+    def codes(q8=A, k8=A, v8=A, sq=A, sk=A, sv=A, o=A, lse=A, B=1, Nq=64, Nk=64, H=2, d=128,
+              qk=0.1, causal=0):
+        return lib.fa_fwd_fp8_codes(q8, k8, v8, sq, sk, sv, o, lse, B, Nq, Nk, H, d, qk, causal, None)
+
+    assert codes(sv=None) == -1 and codes(q8=None) == -1
+    assert codes(d=64) == -3 and codes(Nq=0) == -2 and codes(qk=-1.0) == -3
+    assert codes(o=MIS) == -4 and codes(sk=A + 2) == -4
+
+
+def test_fp8_workspace_bytes():
+    n = fa355.fa_fp8_workspace_bytes(8, 4096, 4096, 16, 128)
+    codes = 3 * 8 * 4096 * 16 * 128
+    assert codes < n < codes + (1 << 20) and n % 256 == 0
+    assert fa355.fa_fp8_workspace_bytes(8, 4096, 4096, 16, 64) == 0
+    assert fa355.fa_fp8_workspace_bytes(0, 4096, 4096, 16, 128) == 0
+
+
 def test_binding_raises_on_error():
     with pytest.raises(fa355.FaError) as e:
         fa355._check(-3)

@@ -1,0 +1,189 @@
+"""The FP8 forward (Hadamard-rotated e4m3) on the GPU against the FP8 oracle.
+
+Bars, per element: O max-abs <= 1e-2 + 2 * slack and LSE max-abs <= 1e-3 +
+2 * slack, where slack (computed by the oracle) bounds to first order what codes
+that sit at a near-tie may move -- P codes (the kernel's exponent is an fp32
+value, the oracle's an fp64 one; relative tie window 2e-4 covers the matrix
+unit's partial-sum rounding seen on gfx950, about 6e-6 of the largest term, times
+|S| up to 30) and, end to end, Q/K codes within twice the fp32 rotation's
+rounding bound of a midpoint.  Away from ties the decisions are the same.
+
+The quantisation itself is checked code by code: the scales are equal and every
+code equals the oracle's, except where the oracle's value lies within the fp32
+rotation bound of a midpoint, where the neighbouring code is accepted.  The
+oracle's inputs never come from the GPU: the attention-stage test uploads
+oracle-made codes.
+"""
+
+import pytest
+import torch
+
+import oracle.fp8 as of8
+from oracle import attention_forward as exact_forward
+from io_aware_exact_attention_amd import fa355, workloads as wl
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+TIE_REL = 2e-4
+DEV = "cuda"
+
+
+def _inputs(B, Nq, Nk, H, seed, outliers=False):
+    x = wl.make_dense(B, Nq, H, 128, seed, Nk=Nk, with_dout=False)
+    if outliers:
+        # two channels of Q and K twenty times larger (the case the rotation is for)
+        for n in ("q", "k"):
+            t = x[n].float()
+            t[..., [5, 77]] *= 20.0
+            x[n] = t.to(torch.bfloat16)
+    x["signs"] = wl.make_signs(128, seed + 1)
+    return x
+
+
+def _check(o, lse, o_ref, lse_ref, so, sl, what):
+    o, lse = gu.f64(o), gu.f64(lse)
+    assert torch.isfinite(o).all(), f"non-finite O {what}"
+    eo = (o - o_ref).abs() - 2 * so
+    el = (lse - lse_ref).abs() - 2 * sl
+    fin = torch.isfinite(lse_ref)
+    assert torch.equal(torch.isfinite(lse), fin), f"LSE finiteness {what}"
+    assert eo.max().item() <= gu.O_TOL, f"O excess {eo.max().item():.3e} {what}"
+    if fin.any():
+        assert el[fin].max().item() <= gu.LSE_TOL, f"LSE excess {el[fin].max().item():.3e} {what}"
+
+
+def _run_full(x, scale, causal, rotate=True):
+    q, k, v = (x[n].to(DEV) for n in ("q", "k", "v"))
+    sg = x["signs"].to(DEV)
+    B, Nq, H, d = q.shape
+    Nk = k.shape[1]
+    ws = torch.empty(fa355.fa_fp8_workspace_bytes(B, Nq, Nk, H, d), dtype=torch.uint8, device=DEV)
+    o = torch.empty_like(q)
+    lse = torch.empty(B, H, Nq, dtype=torch.float32, device=DEV)
+    fa355.fa_fwd_fp8(q, k, v, sg, o, lse, ws, scale, causal, rotate)
+    torch.cuda.synchronize()
+    return o, lse, ws
+
+
+CASES = [
+    # B, Nq, Nk, H, causal
+    (1, 300, 300, 2, True),      # several tiles and a ragged tail
+    (2, 257, 257, 3, False),
+    (1, 64, 64, 1, True),        # exactly one tile
+    (2, 77, 200, 2, False),      # Nq != Nk
+    (1, 1, 1, 2, True),          # a single token
+    (1, 1, 513, 2, False),       # one query, many keys
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "B{}_Nq{}_Nk{}_H{}_{}".format(
+    *c[:4], "causal" if c[4] else "full"))
+def test_fp8_quantisation_codes(case):
+    gu.need_gpu()
+    B, Nq, Nk, H, causal = case
+    gu.announce(f"fp8 quantise B{B} Nq{Nq} Nk{Nk} H{H}")
+    x = _inputs(B, Nq, Nk, H, seed=3000 + Nq + Nk + H)
+    _, _, ws = _run_full(x, 128 ** -0.5, causal)
+    q8, k8, v8, scales = fa355.fp8_workspace_views(ws, B, Nq, Nk, H, 128)
+    for t, (name, sg) in enumerate((("q", x["signs"]), ("k", x["signs"]), ("v", None))):
+        codes_ref, s_ref, scaled = of8.quantize_e4m3(x[name], sg)
+        got = [q8, k8, v8][t].cpu()
+        assert torch.equal(gu.f64(scales[t]), s_ref), f"{name} scales"
+        diff = got != codes_ref
+        if diff.any():
+            assert sg is not None, f"{name}: unrotated values are exact, codes must match"
+            atol = 2.0 * of8.fp32_rotation_error(x[name], sg, s_ref)
+            tie = of8.e4m3_near_tie(scaled, 1e-7, atol)
+            assert bool(tie[diff].all()), f"{name}: {int((diff & ~tie).sum())} codes differ off a tie"
+            # and the accepted ones are the neighbouring code of the same sign
+            dv = (of8.e4m3_decode(got[diff]) - of8.e4m3_decode(codes_ref[diff])).abs()
+            assert bool((dv <= of8.e4m3_step(codes_ref[diff]) + of8.e4m3_step(got[diff])).all())
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "B{}_Nq{}_Nk{}_H{}_{}".format(
+    *c[:4], "causal" if c[4] else "full"))
+def test_fp8_attention_stage(case):
+    # the attention kernel alone, on codes and scales the oracle made
+    gu.need_gpu()
+    B, Nq, Nk, H, causal = case
+    gu.announce(f"fp8 attention codes B{B} Nq{Nq} Nk{Nk} H{H} causal={causal}")
+    x = _inputs(B, Nq, Nk, H, seed=3100 + Nq + Nk + H)
+    q8, sq, _ = of8.quantize_e4m3(x["q"], x["signs"])
+    k8, sk, _ = of8.quantize_e4m3(x["k"], x["signs"])
+    v8, sv, _ = of8.quantize_e4m3(x["v"], None)
+    qk_scale = 128 ** -0.5 / 128
+    o_ref, lse_ref, so, sl = of8.fp8_attention_forward(q8, k8, v8, sq, sk, sv, qk_scale, causal, TIE_REL)
+    dev = [t.to(DEV) for t in (q8, k8, v8)]
+    sc = [t.to(torch.float32).reshape(-1).to(DEV) for t in (sq, sk, sv)]
+    o = torch.empty(B, Nq, H, 128, dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty(B, H, Nq, dtype=torch.float32, device=DEV)
+    fa355.fa_fwd_fp8_codes(*dev, *sc, o, lse, qk_scale, causal)
+    torch.cuda.synchronize()
+    _check(o, lse, o_ref, lse_ref, so, sl, f"codes {case}")
+
+
+@pytest.mark.parametrize("case", CASES[:4], ids=lambda c: "B{}_Nq{}_Nk{}_H{}_{}".format(
+    *c[:4], "causal" if c[4] else "full"))
+@pytest.mark.parametrize("rotate", [True, False], ids=["rotated", "plain"])
+def test_fp8_end_to_end(case, rotate):
+    gu.need_gpu()
+    B, Nq, Nk, H, causal = case
+    gu.announce(f"fp8 end to end B{B} Nq{Nq} Nk{Nk} H{H} causal={causal} rotate={rotate}")
+    x = _inputs(B, Nq, Nk, H, seed=3200 + Nq + Nk + H)
+    scale = 128 ** -0.5
+    o, lse, _ = _run_full(x, scale, causal, rotate)
+    o_ref, lse_ref, so, sl, _, _ = of8.fp8_forward(x["q"], x["k"], x["v"], x["signs"], scale, causal,
+                                                   rotate, TIE_REL, fp32_rotation=True)
+    _check(o, lse, o_ref, lse_ref, so, sl, f"end to end {case} rotate={rotate}")
+
+
+def test_fp8_deterministic():
+    gu.need_gpu()
+    x = _inputs(2, 700, 700, 2, seed=33)
+    a = _run_full(x, 0.088, True)
+    b = _run_full(x, 0.088, True)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+    # the codes and scales (the workspace's padding and block maxima are scratch)
+    for u, w in zip(fa355.fp8_workspace_views(a[2], 2, 700, 700, 2, 128),
+                    fa355.fp8_workspace_views(b[2], 2, 700, 700, 2, 128)):
+        assert torch.equal(u, w)
+
+
+def test_fp8_error_against_exact_and_rotation_helps():
+    # the page's point, on the GPU path: with outlier channels in Q and K, the
+    # rotated FP8 forward is closer to exact attention than the unrotated one
+    gu.need_gpu()
+    gu.announce("fp8 rmse vs exact, outliers")
+    B, N, H = 1, 512, 4
+    scale = 0.02
+    x = _inputs(B, N, N, H, seed=3300, outliers=True)
+    o_ex, _ = exact_forward(x["q"], x["k"], x["v"], scale, True)
+    o_rot = _run_full(x, scale, True, True)[0]
+    o_pl = _run_full(x, scale, True, False)[0]
+    e_rot, e_pl = of8.rmse(o_rot, o_ex), of8.rmse(o_pl, o_ex)
+    print(f"[fp8] rmse vs exact: rotated {e_rot:.3e}, unrotated {e_pl:.3e}", flush=True)
+    assert e_rot < e_pl
+    # and without outliers the FP8 forward stays within a few e4m3 steps of exact
+    y = _inputs(B, N, N, H, seed=3301)
+    o_ex2, _ = exact_forward(y["q"], y["k"], y["v"], 128 ** -0.5, True)
+    e2 = of8.rmse(_run_full(y, 128 ** -0.5, True, True)[0], o_ex2)
+    print(f"[fp8] rmse vs exact, N(0,1) inputs: {e2:.3e}", flush=True)
+    assert e2 < 3e-2
+
+
+def test_fp8_workload_full_size_sampled():
+    # the benchmarked shape at full size; whole (batch, head) slices compared
+    gu.need_gpu()
+    w8 = wl.FP8_WORKLOADS["fp8_b8_h16_n4096_d128_causal"]
+    base = wl.WORKLOADS[w8.base]
+    gu.announce(f"fp8 full size {w8.name}")
+    x = wl.make_inputs(w8.name)
+    o, lse, ws = _run_full(x, base.scale, True)
+    assert torch.isfinite(o).all()
+    for b, h in ((0, 0), (5, 11)):
+        sl_ = slice(h, h + 1)
+        o_ref, lse_ref, so, sl, _, _ = of8.fp8_forward(
+            x["q"][b:b + 1, :, sl_], x["k"][b:b + 1, :, sl_], x["v"][b:b + 1, :, sl_], x["signs"],
+            base.scale, True, True, TIE_REL, fp32_rotation=True)
+        _check(o[b:b + 1, :, sl_], lse[b:b + 1, sl_], o_ref, lse_ref, so, sl, f"full size b{b} h{h}")
