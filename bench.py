@@ -38,15 +38,31 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(ROOT, "io_aware_exact_attention_amd", "csrc")
 
 
-def kernel_source_hash() -> str:
-    """sha256 over the HIP sources (sorted by name): identifies the kernels a
+# The sources that define each path's kernels (their launch shapes come from the
+# configuration structs in the same headers).
+KERNEL_SOURCES = {
+    "bf16": ("fa_device.hpp", "fa_params.hpp", "fa_tiles.hpp", "fa_fwd.hpp", "fa_bwd.hpp"),
+    "decode": ("fa_device.hpp", "fa_params.hpp", "fa_tiles.hpp", "fa_decode.hpp"),
+    "fp8": ("fa_device.hpp", "fa_params.hpp", "fa_tiles.hpp", "fa_fp8.hpp"),
+}
+
+
+def workload_kind(workload: str) -> str:
+    if workload in wl.FP8_WORKLOADS:
+        return "fp8"
+    if workload in wl.DECODE_WORKLOADS:
+        return "decode"
+    return "bf16"
+
+
+def kernel_source_hash(kind: str = "bf16") -> str:
+    """sha256 over the sources of one path's kernels: identifies the kernels a
     stored counter summary was taken from."""
     h = hashlib.sha256()
-    for name in sorted(os.listdir(CSRC)):
-        if name.endswith((".hip", ".hpp")):
-            h.update(name.encode())
-            with open(os.path.join(CSRC, name), "rb") as f:
-                h.update(f.read())
+    for name in KERNEL_SOURCES[kind]:
+        h.update(name.encode())
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
     return h.hexdigest()
 
 
@@ -70,7 +86,7 @@ def measured_traffic(workload: str):
                 calib = (int(t[2]), float(t[4]), float(t[6]))   # bytes, fetch KiB, write KiB
             elif t[0] == "kernel":
                 kern[t[1]] = (float(t[3]), float(t[5]))
-    if src != kernel_source_hash() or calib is None or calib[1] <= 0 or calib[2] <= 0:
+    if src != kernel_source_hash(workload_kind(workload)) or calib is None or calib[1] <= 0 or calib[2] <= 0:
         return None
     fetch_scale = calib[0] / (calib[1] * 1024)
     write_scale = calib[0] / (calib[2] * 1024)
