@@ -72,9 +72,38 @@ struct Fp8AttnParams {
 
 // ------------------------------------------------------------------ quantisation
 
+// Value of lane (lane ^ M) within each row of 16 lanes, through DPP (no LDS):
+// quad permutations for M = 1, 2; "rotate right" by 8 for M = 8; for M = 4 the
+// rotations by 12 (lane + 4) and by 4 (lane - 4), chosen by lane bit 2.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+template <int M>
+__device__ __forceinline__ float xor_lane16(float x, int lane) {
+    if constexpr (M == 1) return dpp_f32<0xB1>(x);    // quad_perm [1, 0, 3, 2]
+    if constexpr (M == 2) return dpp_f32<0x4E>(x);    // quad_perm [2, 3, 0, 1]
+    if constexpr (M == 8) return dpp_f32<0x128>(x);   // row_ror:8
+    if constexpr (M == 4) {
+        const float up = dpp_f32<0x12C>(x);           // row_ror:12 -> lane + 4
+        const float dn = dpp_f32<0x124>(x);           // row_ror:4  -> lane - 4
+        return (lane & 4) ? dn : up;
+    }
+    return x;
+}
+
+// Butterfly across lanes: the lane with bit M clear holds a and gets a + b; its
+// partner holds b and gets a - b, i.e. o + sgn * own with sgn = -1 there.
+template <int M>
+__device__ __forceinline__ void fwht_lane_stage(float* v, int chunk) {
+    const float sgn = (chunk & M) ? -1.f : 1.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = __builtin_fmaf(sgn, v[e], xor_lane16<M>(v[e], chunk));
+}
+
 // 16 threads per 128-element row, 8 consecutive elements each (elements
-// 8 chunk .. 8 chunk + 7, their signs sg[0..7]).  Rotates v[8] in place:
-// y = x diag(sigma) H over the row (fp32 butterflies a + b, a - b).
+// 8 chunk .. 8 chunk + 7, their signs sg[0..7]; chunk = lane % 16).  Rotates v[8]
+// in place: y = x diag(sigma) H over the row (fp32 butterflies a + b, a - b).
 __device__ __forceinline__ void fwht_row8(float* v, const float* sg, int chunk) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) v[e] *= sg[e];
@@ -87,27 +116,31 @@ __device__ __forceinline__ void fwht_row8(float* v, const float* sg, int chunk) 
                 v[e] = a + b;
                 v[e + s] = a - b;
             }
-#pragma unroll
-    for (int m = 1; m < 16; m <<= 1) {
-        const bool hi = (chunk & m) != 0;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float o = __shfl_xor(v[e], m, 64);
-            v[e] = hi ? o - v[e] : v[e] + o;
-        }
-    }
+    fwht_lane_stage<1>(v, chunk);
+    fwht_lane_stage<2>(v, chunk);
+    fwht_lane_stage<4>(v, chunk);
+    fwht_lane_stage<8>(v, chunk);
 }
 
-// Row `row` (< n) of tensor t, chunk `chunk`: 8 values, rotated if asked; zeros past n.
-__device__ __forceinline__ void fp8_load_row8(const Fp8QuantParams& p, int t, int b, int h, int row,
-                                              int chunk, const float* sg, float* v) {
-    const bool live = row < p.n[t];
-    const int rr = live ? row : 0;
-    const bf16* src = p.x[t] + (((int64_t)b * p.n[t] + rr) * p.H + h) * kFp8D + 8 * chunk;
-    const bf16x8 x = load16(src);
+// The 8 rows row0 + r0 + 16 i (i = 0..7) of tensor t at chunk `chunk`, loaded
+// together (8 loads in flight per thread), converted to fp32 and rotated if asked;
+// rows past n read as zeros.
+__device__ __forceinline__ void fp8_load_rows(const Fp8QuantParams& p, int t, int b, int h, int row0,
+                                              int r0, int chunk, const float* sg, float (*v)[8]) {
+    bf16x8 x[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = live ? (float)x[e] : 0.f;
-    if (p.rotate && t < 2) fwht_row8(v, sg, chunk);
+    for (int i = 0; i < 8; ++i) {
+        const int row = row0 + r0 + 16 * i;
+        const int rr = row < p.n[t] ? row : 0;
+        x[i] = load16(p.x[t] + (((int64_t)b * p.n[t] + rr) * p.H + h) * kFp8D + 8 * chunk);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const bool live = row0 + r0 + 16 * i < p.n[t];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[i][e] = live ? (float)x[i][e] : 0.f;
+        if (p.rotate && t < 2) fwht_row8(v[i], sg, chunk);
+    }
 }
 
 __device__ __forceinline__ void fp8_signs8(const Fp8QuantParams& p, int t, int chunk, float* sg) {
@@ -138,12 +171,12 @@ __global__ __launch_bounds__(256) void fp8_amax_kernel(Fp8QuantParams p) {
         const int chunk = threadIdx.x & 15;
         float sg[8];
         fp8_signs8(p, t, chunk, sg);
-        for (int r = threadIdx.x >> 4; r < kFp8QuantRows; r += 16) {
-            float v[8];
-            fp8_load_row8(p, t, b, h, row0 + r, chunk, sg, v);
+        float v[8][8];
+        fp8_load_rows(p, t, b, h, row0, threadIdx.x >> 4, chunk, sg, v);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(v[e]));
-        }
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(v[i][e]));
     }
     mx = block_max256(mx, red);
     if (threadIdx.x == 0) p.amax[((int64_t)t * p.B * p.H + bh) * p.nblk + blk] = mx;
@@ -167,26 +200,29 @@ __global__ __launch_bounds__(256) void fp8_quant_kernel(Fp8QuantParams p) {
     const int nb_t = (p.n[t] + kFp8QuantRows - 1) / kFp8QuantRows;
     const int row0 = blk * kFp8QuantRows;
     if (blk >= nb_t) return;   // uniform over the block
+    const int chunk = threadIdx.x & 15;
+    float sg[8];
+    fp8_signs8(p, t, chunk, sg);
+    float v[8][8];
+    fp8_load_rows(p, t, b, h, row0, threadIdx.x >> 4, chunk, sg, v);
     const float* am = p.amax + ((int64_t)t * p.B * p.H + bh) * p.nblk;
     float mx = 0.f;
     for (int i = threadIdx.x; i < nb_t; i += 256) mx = fmaxf(mx, am[i]);
     mx = block_max256(mx, red);
     const int k = mx > 0.f ? fp8_scale_exp(mx) : 0;
     if (blk == 0 && threadIdx.x == 0) p.scales[t * p.B * p.H + bh] = ldexpf(1.f, k);
-    const int chunk = threadIdx.x & 15;
-    float sg[8];
-    fp8_signs8(p, t, chunk, sg);
-    // the 16 threads of a row share its bound, so the row's shuffles stay within active lanes
-    for (int r = threadIdx.x >> 4; r < kFp8QuantRows && row0 + r < p.n[t]; r += 16) {
-        float v[8];
-        fp8_load_row8(p, t, b, h, row0 + r, chunk, sg, v);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int row = row0 + (threadIdx.x >> 4) + 16 * i;
         int w0 = 0, w1 = 0;
-        w0 = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(v[0], -k), ldexpf(v[1], -k), w0, false);
-        w0 = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(v[2], -k), ldexpf(v[3], -k), w0, true);
-        w1 = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(v[4], -k), ldexpf(v[5], -k), w1, false);
-        w1 = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(v[6], -k), ldexpf(v[7], -k), w1, true);
-        uint8_t* dst = p.codes[t] + (((int64_t)b * p.n[t] + row0 + r) * p.H + h) * kFp8D + 8 * chunk;
-        *reinterpret_cast<i32x2*>(dst) = (i32x2){w0, w1};
+        w0 = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(v[i][0], -k), ldexpf(v[i][1], -k), w0, false);
+        w0 = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(v[i][2], -k), ldexpf(v[i][3], -k), w0, true);
+        w1 = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(v[i][4], -k), ldexpf(v[i][5], -k), w1, false);
+        w1 = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(v[i][6], -k), ldexpf(v[i][7], -k), w1, true);
+        if (row < p.n[t]) {
+            uint8_t* dst = p.codes[t] + (((int64_t)b * p.n[t] + row) * p.H + h) * kFp8D + 8 * chunk;
+            *reinterpret_cast<i32x2*>(dst) = (i32x2){w0, w1};
+        }
     }
 }
 
