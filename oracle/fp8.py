@@ -26,19 +26,20 @@ Readings taken where the pages are silent (each one is a choice, stated):
   an input.  The rotated tensors are kept unnormalised, Qh = Q diag(sigma) H_d
   (likewise Kh), and the 1/d that restores J's normalisation goes into the
   score scale: Qh Kh^T = d Q K^T.  V is not rotated.
-* Scales: one per (batch, head) and tensor, a power of two,
-  s = 2^ceil(log2(amax / 448)) over that head's rotated values (s = 1 when
-  amax = 0); codes = e4m3(x / s).  Dividing by a power of two is exact, so the
-  code depends only on the value x.
-* Scores S = scale * s_q * s_k / d * (q8 . k8), decoded codes.
+* Scales: one per block of 64 consecutive rows of each (batch, head) and
+  tensor, a power of two, s = 2^ceil(log2(amax / 448)) over the block's
+  rotated values (s = 1 when amax = 0); codes = e4m3(x / s).  Dividing by a
+  power of two is exact, so the code depends only on the value x.
+* Scores S_ij = scale * s_q(i) * s_k(j) / d * (q8_i . k8_j), decoded codes;
+  V row j is s_v(j) * v8_j.
 * P~ = exp(S - m) lies in [0, 1]; the P V product uses p8 = e4m3(256 * P~)
-  and O = s_v / 256 * sum_j p8_j v8_j / l, where l = sum_j P~_j is the
+  and O = sum_j p8_j s_v(j) v8_j / (256 l), where l = sum_j P~_j is the
   unquantised row sum; LSE = m + ln(l).  m is the online softmax's running
   maximum over blocks of 64 keys ("08 · FlashAttention", §二), so P~ is rounded
   relative to the maximum seen so far and earlier blocks are rescaled after
   rounding: the one-pass kernel cannot know the final maximum when it rounds.
 
-Layout: q, k, v [B, N, H, d]; codes the same, uint8; scales [B, H]; O
+Layout: q, k, v [B, N, H, d]; codes the same, uint8; scales [B, H, nblk]; O
 [B, Nq, H, d]; LSE [B, H, Nq].
 """
 
@@ -52,6 +53,7 @@ _NEG_INF = float("-inf")
 E4M3_MAX = 448.0
 P_SCALE = 256.0          # P~ in [0, 1] is quantised as e4m3(256 * P~)
 KEY_BLOCK = 64           # keys per block of the online pass (the kernel's key tile)
+QUANT_ROWS = 64          # rows per quantisation scale
 
 
 def _f64(x: torch.Tensor) -> torch.Tensor:
@@ -145,29 +147,49 @@ def rotate(x: torch.Tensor, signs: torch.Tensor) -> torch.Tensor:
     return torch.matmul(x * _f64(signs).reshape(d), hadamard(d))
 
 
-def quantize_e4m3(x: torch.Tensor, signs: torch.Tensor | None = None):
-    """Per-(batch, head) power-of-two scale and e4m3 codes of x (rotated if signs given).
+def quantize_e4m3(x: torch.Tensor, signs: torch.Tensor | None = None,
+                  block_rows: int | None = QUANT_ROWS):
+    """Power-of-two scales and e4m3 codes of x (rotated if signs are given).
 
-    Returns (codes uint8 [B, N, H, d], scales float64 [B, H], scaled float64
-    [B, N, H, d] = the values that were rounded, x / s).
+    One scale per block of ``block_rows`` consecutive rows of each (batch, head)
+    (None: one block of all rows), s = 2^ceil(log2(amax / 448)) over the block's
+    values (1 for an all-zero block).  Returns (codes uint8 [B, N, H, d], scales
+    float64 [B, H, nblk], scaled float64 [B, N, H, d] = x / s, the values that
+    were rounded).
     """
     xr = rotate(x, signs) if signs is not None else _f64(x)
-    amax = xr.abs().amax(dim=(1, 3))                              # [B, H]
+    B, N, H, d = xr.shape
+    rows = N if block_rows is None else int(block_rows)
+    nblk = max(1, -(-N // rows))
+    pad = nblk * rows - N
+    xp = torch.cat([xr, torch.zeros(B, pad, H, d, dtype=torch.float64)], 1) if pad else xr
+    amax = xp.abs().reshape(B, nblk, rows, H, d).amax(dim=(2, 4)).transpose(1, 2)   # [B, H, nblk]
     e = torch.ceil(torch.log2(torch.where(amax > 0, amax, torch.ones_like(amax)) / E4M3_MAX))
     s = torch.where(amax > 0, torch.ldexp(torch.ones_like(amax), e), torch.ones_like(amax))
-    scaled = xr / s[:, None, :, None]
+    scaled = xr / row_scales(s, N, rows).transpose(1, 2)[..., None]
     return e4m3_encode(scaled), s, scaled
+
+
+def row_scales(s: torch.Tensor, n: int, rows: int) -> torch.Tensor:
+    """Per-block scales [B, H, nblk] -> the scale of every row, [B, H, n].
+    Scales given as [B, H] are one block of all rows."""
+    s = _f64(s)
+    if s.dim() == 2:
+        return s[:, :, None].expand(s.shape[0], s.shape[1], n)
+    return s.repeat_interleave(int(rows), dim=2)[:, :, :n]
 
 
 # ------------------------------------------------------------- fp8 attention
 
 def fp8_attention_forward(q8, k8, v8, sq, sk, sv, qk_scale: float, causal: bool,
                           tie_rel: float = 1e-5, q_scaled=None, k_scaled=None, v_scaled=None,
-                          q_tie_atol=0.0, k_tie_atol=0.0, block: int | None = KEY_BLOCK):
+                          q_tie_atol=0.0, k_tie_atol=0.0, block: int | None = KEY_BLOCK,
+                          scale_rows: int = QUANT_ROWS):
     """Attention over decoded e4m3 codes with the P V product on e4m3 probabilities.
 
-    q8 [B, Nq, H, d], k8/v8 [B, Nk, H, d] uint8 codes; sq, sk, sv [B, H] scales;
-    S = qk_scale * sq * sk * (q8 . k8).  The keys are visited in blocks of
+    q8 [B, Nq, H, d], k8/v8 [B, Nk, H, d] uint8 codes; sq, sk, sv [B, H, nblk]
+    scales, one per block of ``scale_rows`` rows; S_ij = qk_scale * sq_i * sk_j *
+    (q8_i . k8_j) and V row j is sv_j * v8_j.  The keys are visited in blocks of
     ``block`` (None: one block) with the online softmax's running maximum m
     ("08 · FlashAttention", §二): per block, P~ = exp(S - m_new) <= 1 is rounded
     as e4m3(256 P~) for the P V product, earlier blocks' sums are rescaled by
@@ -202,11 +224,15 @@ def fp8_attention_forward(q8, k8, v8, sq, sk, sv, qk_scale: float, causal: bool,
 
     tq, tk = tie_steps(q_scaled, q8, q_tie_atol), tie_steps(k_scaled, k8, k_tie_atol)
     tv = tie_steps(v_scaled, v8)
+    rq = row_scales(sq, Nq, scale_rows)                                # [B, H, Nq]
+    rk = row_scales(sk, Nk, scale_rows)
+    rv = row_scales(sv, Nk, scale_rows)
     for b in range(B):
         for h in range(H):
-            c = qk_scale * float(sq[b, h]) * float(sk[b, h])
-            svh = float(sv[b, h])
-            qh, kh, vh = qd[b, :, h], kd[b, :, h], vd[b, :, h]
+            c = qk_scale * torch.outer(rq[b, h], rk[b, h])            # [Nq, Nk]
+            qh, kh = qd[b, :, h], kd[b, :, h]
+            vh = vd[b, :, h] * rv[b, h][:, None]                        # V in its own units
+            tvh = tv[b, :, h] * rv[b, h][:, None]
             s = c * torch.matmul(qh, kh.transpose(0, 1))              # [Nq, Nk]
             # |dS| from Q/K codes at a near-tie flipping by one step
             ds = c * (torch.matmul(tq[b, :, h], kh.abs().transpose(0, 1))
@@ -238,29 +264,30 @@ def fp8_attention_forward(q8, k8, v8, sq, sk, sv, qk_scale: float, causal: bool,
                 to_fin = torch.exp(m_ref - m_fin0)                   # later rescaling of this block
                 tp = e4m3_near_tie(P_SCALE * pt, tie_rel).to(torch.float64) * e4m3_step(p8)
                 tie_p += to_fin * torch.matmul(tp, vh[j0:j0 + bs].abs())
-                tie_v += to_fin * torch.matmul(pq, tv[b, j0:j0 + bs, h])
+                tie_v += to_fin * torch.matmul(pq, tvh[j0:j0 + bs])
             linv = torch.where(live, 1.0 / l, torch.zeros_like(l))
-            o[b, :, h] = svh / P_SCALE * acc * linv
+            o[b, :, h] = acc / P_SCALE * linv
             lse[b, h] = torch.where(live, m + torch.log(l), torch.full_like(m, _NEG_INF)).squeeze(-1)
             # slack: P codes at a near-tie, V codes at a near-tie, and dS (first order)
             p_true = torch.exp(s - m_fin0) * torch.where(live, 1.0 / torch.exp(s - m_fin0).sum(-1, keepdim=True), torch.zeros_like(l))
-            vabs = vh.abs() * svh
-            so = svh / P_SCALE * (tie_p + tie_v) * linv
+            vabs = vh.abs()
+            so = (tie_p + tie_v) / P_SCALE * linv
             dev = torch.matmul(p_true * ds, vabs) + (p_true * ds).sum(-1, keepdim=True) * o[b, :, h].abs()
             slack_o[b, :, h] = so + dev
             slack_l[b, h] = (p_true * ds).sum(dim=-1)
     return o, lse, slack_o, slack_l
 
 
-def fp32_rotation_error(x: torch.Tensor, signs: torch.Tensor, s: torch.Tensor) -> torch.Tensor:
+def fp32_rotation_error(x: torch.Tensor, signs: torch.Tensor, s: torch.Tensor,
+                        block_rows: int = QUANT_ROWS) -> torch.Tensor:
     """Bound on |fp32 rotation - exact| / s per row: a fast Walsh-Hadamard
     transform in fp32 rounds once per butterfly stage, each rounding at most
     2^-24 of a partial sum bounded by the row's L1 norm, log2(d) stages.
-    Returns [B, N, H, 1]."""
+    s: the scales [B, H, nblk] of blocks of block_rows rows.  Returns [B, N, H, 1]."""
     x = _f64(x)
-    d = x.shape[-1]
+    B, N, H, d = x.shape
     l1 = (x * _f64(signs).reshape(d)).abs().sum(dim=-1, keepdim=True)
-    return math.log2(d) * 2.0 ** -24 * l1 / _f64(s)[:, None, :, None]
+    return math.log2(d) * 2.0 ** -24 * l1 / row_scales(s, N, block_rows).transpose(1, 2)[..., None]
 
 
 def fp8_forward(q, k, v, signs, scale: float, causal: bool, rotate_qk: bool = True,

@@ -106,28 +106,37 @@ def pin_rotation_keeps_scores(f):
 
 
 def pin_quantize_scale_and_codes(f):
-    x = _rand((2, 33, 3, 64), 405, 3.0)
+    x = _rand((2, 150, 3, 64), 405, 3.0)
     x[1, :, 2] = 0.0                                    # an all-zero head: scale 1, codes 0
+    x[0, 64:128, 1] *= 1e-3                             # one quiet block gets its own, smaller scale
     sg = _signs(64, 406)
     for signs in (None, sg):
-        codes, s, scaled = f.quantize_e4m3(x, signs)
-        xr = f.rotate(x, signs) if signs is not None else x
-        amax = xr.abs().amax(dim=(1, 3))
-        for b in range(2):
-            for h in range(3):
-                sv = float(s[b, h])
-                if float(amax[b, h]) == 0.0:
-                    assert sv == 1.0 and int(codes[b, :, h].to(torch.int64).abs().max()) in (0, 128)
-                    continue
-                m, e = math.frexp(sv)
-                assert m == 0.5, sv                     # a power of two
-                r = float(amax[b, h]) / sv
-                assert 224.0 < r <= 448.0, r            # the smallest such power
-        dec = f.e4m3_decode(codes) * s[:, None, :, None]
-        # each code within half a step of its value (relative 2^-4, or 2^-10 absolute in subnormals)
-        err = (dec - xr).abs() / s[:, None, :, None]
-        assert bool((err <= torch.maximum(xr.abs() / s[:, None, :, None] / 16, torch.full_like(err, 2.0 ** -10)) * (1 + 1e-12)).all())
-        assert torch.allclose(scaled * s[:, None, :, None], xr, rtol=0, atol=0)
+        for rows in (64, None):
+            codes, s, scaled = f.quantize_e4m3(x, signs, rows)
+            xr = f.rotate(x, signs) if signs is not None else x
+            r = 150 if rows is None else rows
+            nblk = -(-150 // r)
+            assert s.shape == (2, 3, nblk)
+            for b in range(2):
+                for h in range(3):
+                    for k in range(nblk):
+                        amax = xr[b, k * r:(k + 1) * r, h].abs().max().item()
+                        sv = float(s[b, h, k])
+                        if amax == 0.0:
+                            assert sv == 1.0
+                            assert int(codes[b, k * r:(k + 1) * r, h].to(torch.int64).max()) in (0, 128)
+                            continue
+                        m, e = math.frexp(sv)
+                        assert m == 0.5, sv                 # a power of two
+                        assert 224.0 < amax / sv <= 448.0, amax / sv   # the smallest such power
+            if rows == 64 and signs is None:
+                assert float(s[0, 1, 1]) < float(s[0, 1, 0]) / 256
+            srow = f.row_scales(s, 150, r).transpose(1, 2)[..., None]
+            dec = f.e4m3_decode(codes) * srow
+            # each code within half a step of its value (relative 2^-4, or 2^-10 absolute in subnormals)
+            err = (dec - xr).abs() / srow
+            assert bool((err <= torch.maximum(xr.abs() / srow / 16, torch.full_like(err, 2.0 ** -10)) * (1 + 1e-12)).all())
+            assert torch.equal(scaled * srow, xr)
 
 
 def _exact_case(causal):
@@ -193,14 +202,19 @@ def pin_fp8_attention_p_rounding_bound(f):
     v8 = torch.randint(0, 255, (B, N, H, d), generator=g).to(torch.uint8)
     for t in (q8, k8, v8):
         t[(t & 127) == 127] = 0x38                     # no NaN codes
-    sq = torch.full((B, H), 2.0 ** -6, dtype=torch.float64)
-    sk = torch.full((B, H), 2.0 ** -5, dtype=torch.float64)
-    sv = torch.full((B, H), 2.0 ** -3, dtype=torch.float64)
+    # one scale per block of 16 rows, different in every block, head and tensor
+    sq = torch.ldexp(torch.ones(B, H, 3, dtype=torch.float64), torch.tensor([[[-6., -4., -7.], [-5., -6., -8.]]]))
+    sk = torch.ldexp(torch.ones(B, H, 3, dtype=torch.float64), torch.tensor([[[-5., -7., -6.], [-4., -5., -7.]]]))
+    sv = torch.ldexp(torch.ones(B, H, 3, dtype=torch.float64), torch.tensor([[[-3., -1., -4.], [-2., -5., -3.]]]))
+
+    def rows(sc):   # the scale of each row, [B, N, H, 1]
+        return sc.repeat_interleave(16, dim=2)[:, :, :N].transpose(1, 2)[..., None]
+
     for causal in (False, True):
-        o, lse, _, _ = f.fp8_attention_forward(q8, k8, v8, sq, sk, sv, 0.37, causal)
-        qd = f.e4m3_decode(q8) * sq[0, 0]
-        kd = f.e4m3_decode(k8) * sk[0, 0]
-        vd = f.e4m3_decode(v8) * sv[0, 0]
+        o, lse, _, _ = f.fp8_attention_forward(q8, k8, v8, sq, sk, sv, 0.37, causal, scale_rows=16)
+        qd = f.e4m3_decode(q8) * rows(sq)
+        kd = f.e4m3_decode(k8) * rows(sk)
+        vd = f.e4m3_decode(v8) * rows(sv)
         o_ref, lse_ref = dense.attention_forward(qd, kd, vd, 0.37, causal)
         p = dense.attention_probs(qd, kd, 0.37, causal)            # [B, H, N, N]
         bound = torch.einsum("bhij,bjhd->bihd", p / 16 + 2.0 ** -18, vd.abs())

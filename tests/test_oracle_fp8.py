@@ -33,10 +33,16 @@ MUTATIONS = {
     "scale_not_power_of_two": ("s = torch.where(amax > 0, torch.ldexp(torch.ones_like(amax), e), torch.ones_like(amax))",
                                "s = torch.where(amax > 0, amax / E4M3_MAX, torch.ones_like(amax))"),
     "scale_rounds_down": ("e = torch.ceil(torch.log2(", "e = torch.floor(torch.log2("),
-    "scores_missing_k_scale": ("c = qk_scale * float(sq[b, h]) * float(sk[b, h])",
-                               "c = qk_scale * float(sq[b, h])"),
-    "p_scale_not_undone": ("o[b, :, h] = svh / P_SCALE * acc * linv", "o[b, :, h] = svh * acc * linv"),
-    "v_scale_dropped": ("o[b, :, h] = svh / P_SCALE * acc * linv", "o[b, :, h] = 1.0 / P_SCALE * acc * linv"),
+    "scores_missing_k_scale": ("c = qk_scale * torch.outer(rq[b, h], rk[b, h])",
+                               "c = qk_scale * rq[b, h][:, None] * torch.ones_like(rk[b, h])[None, :]"),
+    "scores_scales_swapped": ("c = qk_scale * torch.outer(rq[b, h], rk[b, h])",
+                              "c = qk_scale * torch.outer(rk[b, h][:Nq], rq[b, h][:Nk]) if Nq == Nk else qk_scale * torch.outer(rq[b, h], rk[b, h])"),
+    "block_scales_shifted": ("return s.repeat_interleave(int(rows), dim=2)[:, :, :n]",
+                             "return s.repeat_interleave(int(rows), dim=2)[:, :, 1:n + 1] if s.shape[2] * int(rows) > n else s.repeat_interleave(int(rows), dim=2)[:, :, :n]"),
+    "quantise_per_head": ("rows = N if block_rows is None else int(block_rows)\n    nblk",
+                          "rows = N\n    nblk"),
+    "p_scale_not_undone": ("o[b, :, h] = acc / P_SCALE * linv", "o[b, :, h] = acc * linv"),
+    "v_scale_dropped": ("vh = vd[b, :, h] * rv[b, h][:, None]", "vh = vd[b, :, h]"),
     "p_not_quantised": ("p8 = e4m3_encode(P_SCALE * pt)\n                pq = e4m3_decode(p8)",
                         "p8 = e4m3_encode(P_SCALE * pt)\n                pq = P_SCALE * pt"),
     "p_rounded_at_final_max": ("p8 = e4m3_encode(P_SCALE * pt)\n                pq = e4m3_decode(p8)",
