@@ -167,19 +167,21 @@ int fa_fwd_decode(const void* q, const void* k, const void* v, void* o, float* l
  * the forward with both products on e4m3 operands.  Q and K are first
  * multiplied by the random orthogonal J = diag(signs) H_d / sqrt(d) (H_d the
  * Sylvester Hadamard matrix), which leaves Q K^T unchanged and spreads outlier
- * dimensions before quantisation; V is quantised as it is.  Each (batch, head)
- * of each tensor gets one power-of-two scale s = 2^ceil(log2(amax / 448)) and
- * codes e4m3(x / s) (OCP E4M3, round to nearest even).  The probabilities are
- * quantised as e4m3(256 * exp(S - m)) for the P V product; the row sums use
- * the unrounded values.
+ * dimensions before quantisation; V is quantised as it is.  Each block of 64
+ * rows of each (batch, head) of each tensor gets one power-of-two scale
+ * s = 2^ceil(log2(amax / 448)) and codes e4m3(x / s) (OCP E4M3, round to
+ * nearest even).  The probabilities are quantised as e4m3(256 * exp(S - m)),
+ * m the running maximum over 64-key tiles, for the P V product; the row sums
+ * use the unrounded values.
  *   q [B,Nq,H,d], k, v [B,Nk,H,d], o [B,Nq,H,d] bf16; lse [B,H,Nq] fp32.
  *   d must be 128.  causal needs Nq == Nk.  Inputs must be finite.
  *   signs: device fp32 [d], each +1 or -1 (required when rotate = 1; ignored
  *   when rotate = 0, which quantises Q and K unrotated).
  *   workspace: at least fa_fp8_workspace_bytes(...) bytes, 256-byte aligned;
  *   on return it holds, at offsets rounded up to 256 bytes, the codes of q
- *   [B,Nq,H,d], k and v [B,Nk,H,d] (uint8), then the scales [3][B*H] fp32 (q,
- *   k, v), then per-block maxima (scratch).
+ *   [B,Nq,H,d], k and v [B,Nk,H,d] (uint8), then the scales [3][B*H][nblk]
+ *   fp32 (q, k, v; nblk = ceil(max(Nq, Nk) / 64); entries past a tensor's own
+ *   blocks are unused).
  * Errors as fa_fwd; FA_ERR_UNSUPPORTED for d != 128 or when Nk*H*d bytes reach
  * 2 GiB; FA_ERR_WORKSPACE for a missing or small workspace.
  */
@@ -190,9 +192,11 @@ int fa_fwd_fp8(const void* q, const void* k, const void* v, const float* signs, 
 
 /*
  * The attention stage of fa_fwd_fp8 alone, over caller-supplied e4m3 codes
- * q8 [B,Nq,H,d], k8, v8 [B,Nk,H,d] (uint8, 16-byte aligned) and per-(batch,
- * head) scales sq, sk, sv [B*H] fp32: S = qk_scale * sq * sk * (q8 . k8),
- * O = sv * sum_j e4m3(256 P~_j) v8_j / (256 l).  d must be 128.
+ * q8 [B,Nq,H,d], k8, v8 [B,Nk,H,d] (uint8, 16-byte aligned) and power-of-two
+ * scales per 64-row block, sq [B*H][ceil(Nq/64)], sk, sv [B*H][ceil(Nk/64)]
+ * fp32: S_ij = qk_scale * sq(i) * sk(j) * (q8_i . k8_j),
+ * O_i = sum_j e4m3(256 P~_ij) sv(j) v8_j / (256 l_i).  d must be 128; scales
+ * that are not powers of two give unspecified results.
  */
 int fa_fwd_fp8_codes(const void* q8, const void* k8, const void* v8, const float* sq, const float* sk,
                      const float* sv, void* o, float* lse, int B, int Nq, int Nk, int H, int d,

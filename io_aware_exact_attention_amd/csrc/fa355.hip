@@ -463,8 +463,8 @@ namespace {
 size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Fp8Layout {
-    size_t q8, k8, v8, scales, amax, total;
-    int nblk;
+    size_t q8, k8, v8, scales, total;
+    int nblk;   // 64-row blocks of the longer of q and k: the scales' row stride
 };
 
 Fp8Layout fp8_layout(int B, int Nq, int Nk, int H) {
@@ -475,8 +475,7 @@ Fp8Layout fp8_layout(int B, int Nq, int Nk, int H) {
     L.k8 = L.q8 + round256(bh * Nq * kFp8D);
     L.v8 = L.k8 + round256(bh * Nk * kFp8D);
     L.scales = L.v8 + round256(bh * Nk * kFp8D);
-    L.amax = L.scales + round256(3 * bh * sizeof(float));
-    L.total = L.amax + round256(3 * bh * L.nblk * sizeof(float));
+    L.total = L.scales + round256(3 * bh * L.nblk * sizeof(float));
     return L;
 }
 
@@ -498,8 +497,8 @@ int check_fp8_shape(int B, int Nq, int Nk, int H, int d, float scale, int causal
 }
 
 int launch_fp8_attn(const void* q8, const void* k8, const void* v8, const float* sq, const float* sk,
-                    const float* sv, void* o, float* lse, int B, int Nq, int Nk, int H,
-                    float qk_scale, int causal, hipStream_t s) {
+                    const float* sv, int sq_stride, int sk_stride, void* o, float* lse, int B, int Nq,
+                    int Nk, int H, float qk_scale, int causal, hipStream_t s) {
     Fp8AttnParams p;
     std::memset(&p, 0, sizeof(p));
     p.q8 = static_cast<const uint8_t*>(q8);
@@ -515,6 +514,8 @@ int launch_fp8_attn(const void* q8, const void* k8, const void* v8, const float*
     p.nq = Nq;
     p.nk = Nk;
     p.n_tiles = (Nq + Fp8Cfg::BM - 1) / Fp8Cfg::BM;
+    p.sq_stride = sq_stride;
+    p.sk_stride = sk_stride;
     p.qk_scale_log2 = qk_scale * kLog2e;
     const int grid = p.n_tiles * H * B;
     void* args[] = {&p};
@@ -557,7 +558,6 @@ int fa_fwd_fp8(const void* q, const void* k, const void* v, const float* signs, 
     qp.codes[1] = reinterpret_cast<uint8_t*>(ws + L.k8);
     qp.codes[2] = reinterpret_cast<uint8_t*>(ws + L.v8);
     qp.scales = reinterpret_cast<float*>(ws + L.scales);
-    qp.amax = reinterpret_cast<float*>(ws + L.amax);
     qp.signs = signs;
     qp.n[0] = Nq;
     qp.n[1] = Nk;
@@ -569,13 +569,12 @@ int fa_fwd_fp8(const void* q, const void* k, const void* v, const float* signs, 
     hipStream_t s = static_cast<hipStream_t>(stream);
     void* args[] = {&qp};
     const dim3 qgrid((unsigned)(B * H * L.nblk), 3);
-    if (hipLaunchKernel(reinterpret_cast<const void*>(fp8_amax_kernel), qgrid, dim3(256), args, 0, s) != hipSuccess ||
-        hipLaunchKernel(reinterpret_cast<const void*>(fp8_quant_kernel), qgrid, dim3(256), args, 0, s) != hipSuccess)
+    if (hipLaunchKernel(reinterpret_cast<const void*>(fp8_quant_kernel), qgrid, dim3(256), args, 0, s) != hipSuccess)
         return FA_ERR_LAUNCH;
-    const size_t bh = (size_t)B * H;
+    const size_t plane = (size_t)B * H * L.nblk;
     const float qk_scale = rotate ? scale / (float)d : scale;
-    return launch_fp8_attn(qp.codes[0], qp.codes[1], qp.codes[2], qp.scales, qp.scales + bh,
-                           qp.scales + 2 * bh, o, lse, B, Nq, Nk, H, qk_scale, causal, s);
+    return launch_fp8_attn(qp.codes[0], qp.codes[1], qp.codes[2], qp.scales, qp.scales + plane,
+                           qp.scales + 2 * plane, L.nblk, L.nblk, o, lse, B, Nq, Nk, H, qk_scale, causal, s);
 }
 
 int fa_fwd_fp8_codes(const void* q8, const void* k8, const void* v8, const float* sq, const float* sk,
@@ -587,8 +586,9 @@ int fa_fwd_fp8_codes(const void* q8, const void* k8, const void* v8, const float
     if (!aligned(q8, 16) || !aligned(k8, 16) || !aligned(v8, 16) || !aligned(o, 16) || !aligned(lse, 4) ||
         !aligned(sq, 4) || !aligned(sk, 4) || !aligned(sv, 4))
         return FA_ERR_ALIGN;
-    return launch_fp8_attn(q8, k8, v8, sq, sk, sv, o, lse, B, Nq, Nk, H, qk_scale, causal,
-                           static_cast<hipStream_t>(stream));
+    return launch_fp8_attn(q8, k8, v8, sq, sk, sv, (Nq + kFp8QuantRows - 1) / kFp8QuantRows,
+                           (Nk + kFp8QuantRows - 1) / kFp8QuantRows, o, lse, B, Nq, Nk, H, qk_scale,
+                           causal, static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

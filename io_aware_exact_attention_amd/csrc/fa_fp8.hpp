@@ -9,24 +9,23 @@
 // (x diag(sigma) H, a fast Walsh-Hadamard transform per row) and the 1/d that
 // restores J's normalisation is folded into the score scale.
 //
-// Quantisation (two kernels, one grid over (tensor, batch*head, 128-row block)):
-//   fp8_amax_kernel   rotates Q and K (V is left as it is) and writes each
-//                     block's largest magnitude;
-//   fp8_quant_kernel  reduces its head's block maxima to one power-of-two scale
-//                     s = 2^ceil(log2(amax / 448)) -- the smallest with
-//                     amax / s <= 448, decided exactly from the binary exponent --
-//                     recomputes the rotation and writes the e4m3 codes of x / s
-//                     (exact division) with round-to-nearest-even
-//                     v_cvt_pk_fp8_f32.  No value can exceed 448, so the
-//                     conversion's out-of-range behaviour is never reached.
+// Quantisation (fp8_quant_kernel, one pass; grid over (tensor, batch*head,
+// 64-row block)): rotates Q and K (V is left as it is), reduces the block's
+// largest magnitude to one power-of-two scale s = 2^ceil(log2(amax / 448)) --
+// the smallest with amax / s <= 448, decided exactly from the binary exponent --
+// and writes the e4m3 codes of x / s (exact division) with round-to-nearest-even
+// v_cvt_pk_fp8_f32.  No value can exceed 448, so the conversion's out-of-range
+// behaviour is never reached.
 //
 // Attention over the codes (fa_fwd_fp8_kernel): the bf16 forward's structure
 // with v_mfma_scale_f32_32x32x64_f8f6f4 (e4m3 x e4m3, unit block scales):
 //   S^T = K Q^T: 64-deep k-steps over the head dim (2 per 32x32 block, d = 128);
-//   scores in raw units q8.k8, the exponent scale c = scale*log2(e)*s_q*s_k/d;
-//   P~ * 256 = exp2(S c - m c + 8) is converted to e4m3 in registers and is the
-//   B operand of O^T += V^T P^T, one 64-deep step per 64-key tile; the row sum
-//   l keeps the unrounded values; O = s_v * acc / l, LSE = (m c + log2 l - 8) ln 2.
+//   raw scores q8.k8 times c = scale*log2(e)/d * s_q(wave's block) * s_k(tile)
+//   give the base-2 exponent; the running max m is kept in those units;
+//   P~ * 256 = exp2(S c - m + 8) is converted to e4m3 in registers and is the
+//   B operand of O^T += V^T P^T, one 64-deep step per 64-key tile, with the
+//   tile's V scale applied by the MFMA's own power-of-two scale operand; the row
+//   sum l keeps the unrounded values; O = acc / l, LSE = (m + log2 l - 8) ln 2.
 //
 // gfx950 layouts (measured): the 32x32x64 f8 operands give lane l (half
 // h = l / 32) row or column l % 32 and the 32 bytes k = 32h .. 32h + 31; the
@@ -44,16 +43,15 @@ typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kFp8D = 128;          // head dim of the FP8 path
-constexpr int kFp8QuantRows = 128;  // rows per quantisation block
+constexpr int kFp8QuantRows = 64;   // rows per quantisation block (= the key tile)
 
 struct Fp8QuantParams {
     const bf16* x[3];      // q, k, v [B, N_t, H, 128] bf16
     uint8_t* codes[3];     // same layout, e4m3
-    float* scales;         // [3][B*H] powers of two
-    float* amax;           // [3][B*H][nblk] block maxima
+    float* scales;         // [3][B*H][nblk] powers of two, one per 64-row block
     const float* signs;    // [128] +1 / -1
     int n[3];              // rows per batch entry of each tensor
-    int B, H, nblk;        // nblk = blocks of the longest tensor
+    int B, H, nblk;        // nblk = blocks of the longest tensor (the scales' row stride)
     int rotate;            // rotate q and k (tensors 0 and 1)
 };
 
@@ -61,12 +59,12 @@ struct Fp8AttnParams {
     const uint8_t* q8;
     const uint8_t* k8;
     const uint8_t* v8;
-    const float* sq;       // [B*H]
-    const float* sk;
-    const float* sv;
+    const float* sq;       // [B*H][sq_stride], one per 64-row block of q
+    const float* sk;       // [B*H][sk_stride], one per 64-row block (= key tile) of k
+    const float* sv;       // same layout as sk
     bf16* o;               // [B, Nq, H, 128]
     float* lse;            // [B, H, Nq]
-    int batch, H, nq, nk, n_tiles;
+    int batch, H, nq, nk, n_tiles, sq_stride, sk_stride;
     float qk_scale_log2;   // scale * log2(e) (/ d when Q and K were rotated)
 };
 
@@ -122,20 +120,21 @@ __device__ __forceinline__ void fwht_row8(float* v, const float* sg, int chunk) 
     fwht_lane_stage<8>(v, chunk);
 }
 
-// The 8 rows row0 + r0 + 16 i (i = 0..7) of tensor t at chunk `chunk`, loaded
-// together (8 loads in flight per thread), converted to fp32 and rotated if asked;
+// The R rows row0 + r0 + 16 i (i < R) of tensor t at chunk `chunk`, loaded
+// together (R loads in flight per thread), converted to fp32 and rotated if asked;
 // rows past n read as zeros.
+template <int R>
 __device__ __forceinline__ void fp8_load_rows(const Fp8QuantParams& p, int t, int b, int h, int row0,
                                               int r0, int chunk, const float* sg, float (*v)[8]) {
-    bf16x8 x[8];
+    bf16x8 x[R];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < R; ++i) {
         const int row = row0 + r0 + 16 * i;
         const int rr = row < p.n[t] ? row : 0;
         x[i] = load16(p.x[t] + (((int64_t)b * p.n[t] + rr) * p.H + h) * kFp8D + 8 * chunk);
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < R; ++i) {
         const bool live = row0 + r0 + 16 * i < p.n[t];
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[i][e] = live ? (float)x[i][e] : 0.f;
@@ -158,30 +157,6 @@ __device__ __forceinline__ float block_max256(float x, float* red) {
     return x;
 }
 
-// grid (B*H*nblk, 3), 256 threads
-__global__ __launch_bounds__(256) void fp8_amax_kernel(Fp8QuantParams p) {
-    __shared__ float red[4];
-    const int t = blockIdx.y;
-    const int blk = blockIdx.x % p.nblk;
-    const int bh = blockIdx.x / p.nblk;
-    const int b = bh / p.H, h = bh % p.H;
-    const int row0 = blk * kFp8QuantRows;
-    float mx = 0.f;
-    if (row0 < p.n[t]) {
-        const int chunk = threadIdx.x & 15;
-        float sg[8];
-        fp8_signs8(p, t, chunk, sg);
-        float v[8][8];
-        fp8_load_rows(p, t, b, h, row0, threadIdx.x >> 4, chunk, sg, v);
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(v[i][e]));
-    }
-    mx = block_max256(mx, red);
-    if (threadIdx.x == 0) p.amax[((int64_t)t * p.B * p.H + bh) * p.nblk + blk] = mx;
-}
-
 // Exponent k of the smallest power of two with amax / 2^k <= 448 (amax > 0):
 // amax = f 2^E with f in [0.5, 1) and 448 = 0.875 * 2^9.
 __device__ __forceinline__ int fp8_scale_exp(float amax) {
@@ -190,29 +165,31 @@ __device__ __forceinline__ int fp8_scale_exp(float amax) {
     return f <= 0.875f ? E - 9 : E - 8;
 }
 
-// grid (B*H*nblk, 3), 256 threads
+// grid (B*H*nblk, 3), 256 threads: 64 rows x 16 chunks, 4 rows per thread
 __global__ __launch_bounds__(256) void fp8_quant_kernel(Fp8QuantParams p) {
+    constexpr int R = kFp8QuantRows / 16;
     __shared__ float red[4];
     const int t = blockIdx.y;
     const int blk = blockIdx.x % p.nblk;
     const int bh = blockIdx.x / p.nblk;
     const int b = bh / p.H, h = bh % p.H;
-    const int nb_t = (p.n[t] + kFp8QuantRows - 1) / kFp8QuantRows;
     const int row0 = blk * kFp8QuantRows;
-    if (blk >= nb_t) return;   // uniform over the block
+    if (row0 >= p.n[t]) return;   // uniform over the block
     const int chunk = threadIdx.x & 15;
     float sg[8];
     fp8_signs8(p, t, chunk, sg);
-    float v[8][8];
-    fp8_load_rows(p, t, b, h, row0, threadIdx.x >> 4, chunk, sg, v);
-    const float* am = p.amax + ((int64_t)t * p.B * p.H + bh) * p.nblk;
+    float v[R][8];
+    fp8_load_rows<R>(p, t, b, h, row0, threadIdx.x >> 4, chunk, sg, v);
     float mx = 0.f;
-    for (int i = threadIdx.x; i < nb_t; i += 256) mx = fmaxf(mx, am[i]);
+#pragma unroll
+    for (int i = 0; i < R; ++i)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(v[i][e]));
     mx = block_max256(mx, red);
     const int k = mx > 0.f ? fp8_scale_exp(mx) : 0;
-    if (blk == 0 && threadIdx.x == 0) p.scales[t * p.B * p.H + bh] = ldexpf(1.f, k);
+    if (threadIdx.x == 0) p.scales[((int64_t)t * p.B * p.H + bh) * p.nblk + blk] = ldexpf(1.f, k);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < R; ++i) {
         const int row = row0 + (threadIdx.x >> 4) + 16 * i;
         int w0 = 0, w1 = 0;
         w0 = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(v[i][0], -k), ldexpf(v[i][1], -k), w0, false);
@@ -279,13 +256,21 @@ __device__ __forceinline__ f32x16 mfma_fp8_32x32x64(i32x8 a, i32x8 b, f32x16 c) 
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
 
+// The same with A's products scaled by 2^(ea - 127) in the matrix unit (e8m0
+// block-scale operand; measured: exact powers of two).
+__device__ __forceinline__ f32x16 mfma_fp8_32x32x64_scale_a(i32x8 a, i32x8 b, f32x16 c, int ea) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, ea, 0, 127);
+}
+
 __device__ __forceinline__ i32x2 lds_read_tr8(const FA_LDS char* p) {
     return __builtin_amdgcn_ds_read_tr8_b64_v2i32(
         reinterpret_cast<FA_LDS i32x2*>(const_cast<FA_LDS char*>(p)));
 }
 
+// 3 work-groups per CU (12 waves): at most 168 VGPRs and 3 x 32 KB of LDS
+// (measured 14% faster than 2 per CU)
 template <bool CAUSAL>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3)))
 void fa_fwd_fp8_kernel(Fp8AttnParams p) {
     using C = Fp8Cfg;
     __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
@@ -331,9 +316,12 @@ void fa_fwd_fp8_kernel(Fp8AttnParams p) {
     for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[cb][r] = 0.f;
-    float m = kNegInf;   // running max of raw scores q8.k8
+    float m = kNegInf;   // running max of the base-2 exponents S c
     float l = 0.f;       // running sum of 256 P~ over the keys this lane holds
-    const float c = p.qk_scale_log2 * p.sq[bh] * p.sk[bh];
+    const int nbq = (nq + kFp8QuantRows - 1) / kFp8QuantRows;
+    const float c0 = p.qk_scale_log2 * p.sq[(int64_t)bh * p.sq_stride + min(qw0 / kFp8QuantRows, nbq - 1)];
+    const float* skh = p.sk + (int64_t)bh * p.sk_stride;
+    const float* svh = p.sv + (int64_t)bh * p.sk_stride;
 
     // transposed V reads: lane (h2, group half gh, i = lane % 16) names key row
     // 16 rho + 4 h2 + 8 ((i/2) >> 2) + ((i/2) & 3) and byte 8 (i & 1) of chunk 2 cb + gh
@@ -357,6 +345,8 @@ void fa_fwd_fp8_kernel(Fp8AttnParams p) {
         }
         const int kv0 = t * C::BN;
         if (CAUSAL && kv0 > qw0 + 31) continue;
+        const float c = c0 * skh[t];                               // key tile t = scale block t
+        const int ev = 127 + __builtin_amdgcn_frexp_expf(svh[t]) - 1;   // s_v = 2^(ev - 127)
 
         f32x16 s[2];
 #pragma unroll
@@ -388,11 +378,11 @@ void fa_fwd_fp8_kernel(Fp8AttnParams p) {
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-        mx = max_halves(mx);
+        mx = max_halves(mx) * c;
         const float m_new = fmaxf(m, mx);
         const float m_ref = (m_new == kNegInf) ? 0.f : m_new;
-        const float alpha = fast_exp2((m - m_ref) * c);
-        const float off = 8.f - m_ref * c;   // exp2(8) = 256: P~ * 256 in e4m3's range
+        const float alpha = fast_exp2(m - m_ref);
+        const float off = 8.f - m_ref;   // exp2(8) = 256: P~ * 256 in e4m3's range
         float rs = 0.f;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
@@ -434,12 +424,13 @@ void fa_fwd_fp8_kernel(Fp8AttnParams p) {
             }
             const i32x4 a01 = __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3);
             const i32x4 a23 = __builtin_shufflevector(part[2], part[3], 0, 1, 2, 3);
-            acc[cb] = mfma_fp8_32x32x64(__builtin_shufflevector(a01, a23, 0, 1, 2, 3, 4, 5, 6, 7), pk, acc[cb]);
+            acc[cb] = mfma_fp8_32x32x64_scale_a(__builtin_shufflevector(a01, a23, 0, 1, 2, 3, 4, 5, 6, 7), pk,
+                                                acc[cb], ev);
         }
     }
 
     const float lt = sum_halves(l);
-    const float inv = lt > 0.f ? p.sv[bh] / lt : 0.f;
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
     if (qi < nq) {
         bf16* optr = p.o + ((int64_t)b * nq + qi) * tok + h * kFp8D;
 #pragma unroll
@@ -452,7 +443,7 @@ void fa_fwd_fp8_kernel(Fp8AttnParams p) {
             }
         if (h2 == 0) {
             p.lse[((int64_t)b * p.H + h) * nq + qi] =
-                lt > 0.f ? (m * c + __builtin_amdgcn_logf(lt) - 8.f) * kLn2 : kNegInf;
+                lt > 0.f ? (m + __builtin_amdgcn_logf(lt) - 8.f) * kLn2 : kNegInf;
         }
     }
 }

@@ -193,7 +193,8 @@ def fa_fwd_fp8(q, k, v, signs, o, lse, workspace, scale: float, causal: bool, ro
 
 
 def fa_fwd_fp8_codes(q8, k8, v8, sq, sk, sv, o, lse, qk_scale: float, causal: bool, stream=None):
-    """q8 [B,Nq,H,d], k8, v8 [B,Nk,H,d] uint8 e4m3 codes; sq, sk, sv [B*H] fp32."""
+    """q8 [B,Nq,H,d], k8, v8 [B,Nk,H,d] uint8 e4m3 codes; sq [B*H*ceil(Nq/64)], sk, sv
+    [B*H*ceil(Nk/64)] fp32 power-of-two scales, one per 64-row block."""
     B, Nq, H, d = q8.shape
     Nk = k8.shape[1]
     _check(lib().fa_fwd_fp8_codes(_ptr(q8), _ptr(k8), _ptr(v8), _ptr(sq), _ptr(sk), _ptr(sv),
@@ -204,8 +205,9 @@ def fa_fwd_fp8_codes(q8, k8, v8, sq, sk, sv, o, lse, qk_scale: float, causal: bo
 def fp8_workspace_views(workspace, B: int, Nq: int, Nk: int, H: int, d: int):
     """The codes and scales fa_fwd_fp8 leaves in its workspace (views, no copies).
 
-    Offsets follow the documented layout: q8, k8, v8, then scales [3, B*H], each
-    start rounded up to 256 bytes.
+    Offsets follow the documented layout: q8, k8, v8, then scales [3, B, H, nblk]
+    (one per 64-row block, nblk for the longer of q and k), each start rounded up
+    to 256 bytes.
     """
     def up(x):
         return (x + 255) // 256 * 256
@@ -217,7 +219,8 @@ def fp8_workspace_views(workspace, B: int, Nq: int, Nk: int, H: int, d: int):
     q8 = w[:bh * Nq * d].view(B, Nq, H, d)
     k8 = w[o_k:o_k + bh * Nk * d].view(B, Nk, H, d)
     v8 = w[o_v:o_v + bh * Nk * d].view(B, Nk, H, d)
-    scales = w[o_s:o_s + 12 * bh].view(torch.float32).view(3, B, H)
+    nblk = (max(Nq, Nk) + 63) // 64
+    scales = w[o_s:o_s + 12 * bh * nblk].view(torch.float32).view(3, B, H, nblk)
     return q8, k8, v8, scales
 
 
