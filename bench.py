@@ -100,6 +100,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=wl.HEADLINE)
+    ap.add_argument("--forward", choices=("tiles", "persistent"), default="tiles",
+                    help="forward kernel of the dense step: one work-group per tile (fa_fwd) or the "
+                         "persistent longest-first kernel (fa_fwd_persistent)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="wall-time budget of the CPU oracle sample (0 disables it)")
     return ap.parse_args()
@@ -475,9 +478,12 @@ def main():
     ws = torch.empty(fa355.fa_bwd_workspace_bytes(B, H, N, d) // 4, dtype=torch.float32, device=dev)
     scale = w.scale
 
-    names = ["fa_fwd_kernel", "fa_bwd_dot_kernel", "fa_bwd_dkdv_kernel", "fa_bwd_dq_kernel"]
+    persistent = args.forward == "persistent"
+    names = ["fa_fwd_persistent_kernel" if persistent else "fa_fwd_kernel", "fa_bwd_dot_kernel",
+             "fa_bwd_dkdv_kernel", "fa_bwd_dq_kernel"]
+    fwd = fa355.fa_fwd_persistent if persistent else fa355.fa_fwd
     calls = [
-        lambda: fa355.fa_fwd(q, k, v, o, lse, scale, causal),
+        lambda: fwd(q, k, v, o, lse, scale, causal),
         lambda: fa355.fa_bwd_dot(o, do, lse, ws),
         lambda: fa355.fa_bwd_dkdv(q, k, v, do, ws, dk, dv, scale, causal),
         lambda: fa355.fa_bwd_dq(q, k, v, do, ws, dq, scale, causal),
@@ -559,7 +565,7 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": w.name, "B": B, "H": H, "N": N, "d": d, "causal": causal,
-                   "scale": scale},
+                   "scale": scale, "forward": args.forward},
         "fwd_tflops": round(fwd_tf, 2),
         "fwd_pct_peak": round(100 * fwd_tf / PEAK_BF16_TFLOPS, 2),
         "fwd_bwd_tflops_kernels": round(fb_tf_events, 2),

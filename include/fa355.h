@@ -75,6 +75,18 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            int B, int H, int Nq, int Nk, int d, float scale, int causal, void* stream);
 
 /*
+ * Forward, dense batch, as a persistent kernel ("LLM Systems 22: Flash
+ * Attention", §4.1.4 Persistent Kernels, §4.1.5 Load Balancing: longest-
+ * processing-time first): a fixed grid of about as many work-groups as the CUs
+ * hold at once loops over the query tiles, taken longest first (every pair's
+ * tile with the most causal keys, then the next, ...), each XCD working on its
+ * own (batch, head) pairs.  Arguments, results and errors as fa_fwd; the
+ * outputs are bitwise those of fa_fwd (the same tile computation).
+ */
+int fa_fwd_persistent(const void* q, const void* k, const void* v, void* o, float* lse,
+                      int B, int H, int Nq, int Nk, int d, float scale, int causal, void* stream);
+
+/*
  * Forward, packed variable-length batch ("08 · FlashAttention", §四: packing
  * with cu_seqlens instead of a padding mask).
  *   cu_seqlens_q, cu_seqlens_k: int32 device arrays of nseq+1 prefix offsets,

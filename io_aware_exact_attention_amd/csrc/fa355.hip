@@ -226,6 +226,37 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
     return launch_fwd<false>(p, d, causal, static_cast<hipStream_t>(stream));
 }
 
+int fa_fwd_persistent(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                      int Nq, int Nk, int d, float scale, int causal, void* stream) {
+    if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+    if (B <= 0 || Nq <= 0 || Nk <= 0) return FA_ERR_SHAPE;
+    int st = check_common(H, d, scale, causal);
+    if (st) return st;
+    if (causal && Nq != Nk) return FA_ERR_UNSUPPORTED;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
+        return FA_ERR_ALIGN;
+    const int ntq = (Nq + FwdCfg<128>::BM - 1) / FwdCfg<128>::BM;
+    st = check_sizes((int64_t)B * Nq, (int64_t)B * Nk, Nq, Nk, H, d, (int64_t)ntq * H * B);
+    if (st) return st;
+    AttnParams p = base_params(q, k, v, B, H, Nq, Nk, scale);
+    p.o = static_cast<bf16*>(o);
+    p.lse = lse;
+    p.n_tiles = ntq;
+    // a grid the CUs hold at once (2 work-groups per CU), a multiple of the 8 XCDs
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        return FA_ERR_LAUNCH;
+    const int64_t items = (int64_t)ntq * H * B;
+    const int grid = (int)std::max<int64_t>(8, std::min<int64_t>((int64_t)(2 * cus) / 8 * 8, (items + 7) / 8 * 8));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (d == 64)
+        return causal ? launch(fa_fwd_persistent_kernel<64, true>, grid, 256, s, p)
+                      : launch(fa_fwd_persistent_kernel<64, false>, grid, 256, s, p);
+    return causal ? launch(fa_fwd_persistent_kernel<128, true>, grid, 256, s, p)
+                  : launch(fa_fwd_persistent_kernel<128, false>, grid, 256, s, p);
+}
+
 int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
                   const int* cu_seqlens_q, const int* cu_seqlens_k, int nseq, int max_seqlen_q,
                   int max_seqlen_k, int H, int d, float scale, int causal, void* stream) {

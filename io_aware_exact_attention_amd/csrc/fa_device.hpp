@@ -135,4 +135,19 @@ __device__ __forceinline__ void xcd_work_item(int id, int n_tiles, int bh_count,
     rank = L % n_tiles;
 }
 
+// Item `id` of the longest-first order: rank-major (rank 0 = each pair's
+// longest tile), pairs dealt over the 8 XCDs as in xcd_work_item when bh_count
+// is a multiple of 8 (item id runs on XCD id % 8 when the grid is a multiple of 8).
+__device__ __forceinline__ void lpt_work_item(int id, int n_tiles, int bh_count, int& bh, int& rank) {
+    if ((bh_count & 7) == 0) {
+        const int per = bh_count >> 3;   // pairs per XCD
+        const int j = id >> 3;
+        bh = (j % per) * 8 + (id & 7);
+        rank = j / per;
+        return;
+    }
+    bh = id % bh_count;
+    rank = id / bh_count;
+}
+
 }  // namespace fa355

@@ -45,20 +45,16 @@ struct FwdCfg {
     static constexpr int LDS_BYTES = 2 * 2 * TILE_BYTES;   // [buffer][K | V]
 };
 
+// One work item: query tile `tile` of (batch or sequence, head) pair `bh`, with
+// the work-group's LDS at `smem`.
 template <int D, bool CAUSAL, bool VARLEN>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void fa_fwd_kernel(AttnParams p) {
+__device__ __forceinline__ void fwd_tile(const AttnParams& p, char* smem, int bh, int tile) {
     using C = FwdCfg<D>;
-    __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
-
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int h2 = lane >> 5;
     const int col = lane & 31;
 
-    int bh, rank;
-    xcd_work_item(blockIdx.x, p.n_tiles, p.H * p.batch, bh, rank);
-    const int tile = p.n_tiles - 1 - rank;   // longest causal rows first
     const int h = bh % p.H;
     const int b = bh / p.H;
     int qs, nq, ks, nk;
@@ -207,6 +203,39 @@ void fa_fwd_kernel(AttnParams p) {
             p.lse[((int64_t)b * p.H + h) * p.nq + qi] =
                 lt > 0.f ? (m * c + __builtin_amdgcn_logf(lt)) * kLn2 : kNegInf;
         }
+    }
+}
+
+// One work-group per query tile, in the order xcd_work_item gives.
+template <int D, bool CAUSAL, bool VARLEN>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void fa_fwd_kernel(AttnParams p) {
+    __shared__ __attribute__((aligned(1024))) char smem[FwdCfg<D>::LDS_BYTES];
+    int bh, rank;
+    xcd_work_item(blockIdx.x, p.n_tiles, p.H * p.batch, bh, rank);
+    fwd_tile<D, CAUSAL, VARLEN>(p, smem, bh, p.n_tiles - 1 - rank);   // longest causal rows first
+}
+
+// Persistent form ("LLM Systems 22: Flash Attention", §4.1.4 persistent kernels,
+// §4.1.5 longest-processing-time-first): a fixed grid (a multiple of 8, about
+// the number of work-groups the CUs hold at once) loops over the work items.
+// Items are numbered longest first -- all pairs' last query tile (the one with
+// the most causal keys), then all second-to-last ones, ... -- with item i on
+// XCD i % 8 taking pairs bh = i % 8 (mod 8), so each XCD's L2 sees only its
+// own heads; work-group g takes items g, g + grid, g + 2 grid, ...: the sorted
+// list dealt round-robin, which for these equal-length tiles keeps every
+// work-group within one item of the longest-first greedy assignment.
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void fa_fwd_persistent_kernel(AttnParams p) {
+    __shared__ __attribute__((aligned(1024))) char smem[FwdCfg<D>::LDS_BYTES];
+    const int bh_count = p.H * p.batch;
+    const int total = p.n_tiles * bh_count;
+    for (int it = blockIdx.x; it < total; it += gridDim.x) {
+        int bh, rank;
+        lpt_work_item(it, p.n_tiles, bh_count, bh, rank);
+        fwd_tile<D, CAUSAL, false>(p, smem, bh, p.n_tiles - 1 - rank);
+        __syncthreads();   // the next item's loads reuse the LDS buffers
     }
 }
 

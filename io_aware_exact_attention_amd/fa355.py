@@ -29,6 +29,7 @@ _SIGNATURES = {
     "fa_status_string": (ctypes.c_char_p, [_c_int]),
     "fa_version": (_c_int, []),
     "fa_fwd": (_c_int, [_vp] * 5 + [_c_int] * 5 + [_c_float, _c_int, _vp]),
+    "fa_fwd_persistent": (_c_int, [_vp] * 5 + [_c_int] * 5 + [_c_float, _c_int, _vp]),
     "fa_fwd_varlen": (_c_int, [_vp] * 7 + [_c_int] * 5 + [_c_float, _c_int, _vp]),
     "fa_bwd_workspace_bytes": (_sz, [_c_int] * 4),
     "fa_bwd": (_c_int, [_vp] * 10 + [_sz] + [_c_int] * 5 + [_c_float, _c_int, _vp]),
@@ -107,6 +108,12 @@ def fa_fwd(q, k, v, o, lse, scale: float, causal: bool, stream=None):
     B, H, Nq, Nk, d = _dense_dims(q, k)
     _check(lib().fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Nq, Nk, d,
                         float(scale), int(bool(causal)), _stream(stream)))
+
+
+def fa_fwd_persistent(q, k, v, o, lse, scale: float, causal: bool, stream=None):
+    B, H, Nq, Nk, d = _dense_dims(q, k)
+    _check(lib().fa_fwd_persistent(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Nq, Nk, d,
+                                   float(scale), int(bool(causal)), _stream(stream)))
 
 
 def fa_bwd_workspace_bytes(batch_or_nseq: int, H: int, nq: int, d: int) -> int:

@@ -23,6 +23,15 @@ Parity status of each function (what pins it, see ``tests/test_oracle_pins.py``)
   an explicit bottom-right mask, one query token = no mask).
 * ``decode_split_partials`` / ``merge_splits``: pinned (any key split merged
   equals the one-shot result; the merge is associative).
+* ``oracle.fp8`` (FP8 forward with the Hadamard rotation: e4m3 codec,
+  rotation, per-block quantisation, attention with P rounded per key block):
+  pinned (format values, nearest-code search, scipy's Hadamard, score
+  invariance, exact power-of-two cases against the dense oracle, a worked
+  running-max example, the rounding bound, the rotation's benefit), see
+  ``tests/pins_fp8.py``.
+* ``oracle.schedule`` (greedy list scheduling and LPT): pinned to the page's
+  worked example (``tests/golden/lpt_example.json``), brute-force optima and
+  Graham's bounds, see ``tests/test_schedule.py``.
 """
 
 from .attention import (  # noqa: F401
