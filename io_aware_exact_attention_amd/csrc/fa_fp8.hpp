@@ -329,24 +329,33 @@ void fa_fwd_fp8_kernel(Fp8AttnParams p) {
     const int gh = (lane >> 4) & 1;
     const int trow = 4 * h2 + 8 * ((gi >> 1) >> 2) + ((gi >> 1) & 3);
 
+    i32x8 pk = {};   // P^T operand of the current tile
     if (n_kv > 0) {
         loader.load(ldsb, kbase, kv_bytes, 0, wave_s);
         loader.load(ldsb + C::TILE_BYTES, vbase, kv_bytes, 0, wave_s);
     }
+    // the key and value scales of tile t (= scale block t) are fetched one tile
+    // ahead, before that tile's loads, so that waiting for them never waits for
+    // the next tile's K/V loads
+    float sk_next = n_kv > 0 ? skh[0] : 1.f;
+    float sv_next = n_kv > 0 ? svh[0] : 1.f;
     for (int t = 0; t < n_kv; ++t) {
         const FA_LDS char* kt = ldsb + (t & 1) * 2 * C::TILE_BYTES;
         const FA_LDS char* vt = kt + C::TILE_BYTES;
         wait_vmem();
         __syncthreads();
+        const float sk_t = sk_next, sv_t = sv_next;
         if (t + 1 < n_kv) {
+            sk_next = skh[t + 1];
+            sv_next = svh[t + 1];
             FA_LDS char* kn = ldsb + ((t + 1) & 1) * 2 * C::TILE_BYTES;
             loader.load(kn, kbase, kv_bytes, (t + 1) * C::BN * row_bytes, wave_s);
             loader.load(kn + C::TILE_BYTES, vbase, kv_bytes, (t + 1) * C::BN * row_bytes, wave_s);
         }
         const int kv0 = t * C::BN;
         if (CAUSAL && kv0 > qw0 + 31) continue;
-        const float c = c0 * skh[t];                               // key tile t = scale block t
-        const int ev = 127 + __builtin_amdgcn_frexp_expf(svh[t]) - 1;   // s_v = 2^(ev - 127)
+        const float c = c0 * sk_t;
+        const int ev = 127 + __builtin_amdgcn_frexp_expf(sv_t) - 1;   // s_v = 2^(ev - 127)
 
         f32x16 s[2];
 #pragma unroll
@@ -401,13 +410,13 @@ void fa_fwd_fp8_kernel(Fp8AttnParams p) {
                 for (int r = 0; r < 16; ++r) acc[cb][r] *= alpha;
         }
 
-        // P^T operand: byte 16 kb + r = register r of key block kb
-        i32x8 pk;
+        // P^T operand: byte 16 kb + r = register r of key block kb.  The two
+        // conversions overwrite both halves of the word, so the previous tile's
+        // word serves as the "old" input (no zeroing move).
 #pragma unroll
         for (int w = 0; w < 8; ++w) {
             const int kb = w >> 2, r0 = 4 * (w & 3);
-            int x = 0;
-            x = __builtin_amdgcn_cvt_pk_fp8_f32(s[kb][r0], s[kb][r0 + 1], x, false);
+            int x = __builtin_amdgcn_cvt_pk_fp8_f32(s[kb][r0], s[kb][r0 + 1], pk[w], false);
             x = __builtin_amdgcn_cvt_pk_fp8_f32(s[kb][r0 + 2], s[kb][r0 + 3], x, true);
             pk[w] = x;
         }
