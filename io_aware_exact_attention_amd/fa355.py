@@ -1,15 +1,17 @@
 """Python binding of libfa355 (ctypes).  Argument marshalling only.
 
-The functions named like the C entry points (``fa_fwd``, ``fa_bwd``,
-``fa_fwd_varlen``, ``fa_bwd_varlen``, ``fa_bwd_workspace_bytes``,
-``fa_status_string``) take torch tensors that already live on the GPU, pass
-their device pointers and sizes to the library on the current torch stream,
-and raise ``FaError`` on a non-zero status.  Every computation happens in the
-library's HIP kernels; there is no other code path, and a missing or
-unloadable library raises immediately.
+The functions named like the C entry points (``fa_fwd``, ``fa_fwd_persistent``,
+``fa_bwd`` and its stages ``fa_bwd_dot`` / ``fa_bwd_dkdv`` / ``fa_bwd_dq``,
+``fa_fwd_varlen``, ``fa_bwd_varlen``, ``fa_fwd_decode``, ``fa_fwd_fp8``,
+``fa_fwd_fp8_codes``, the ``*_workspace_bytes`` queries, ``fa_status_string``)
+take torch tensors that already live on the GPU, pass their device pointers and
+sizes to the library on the current torch stream, and raise ``FaError`` on a
+non-zero status.  Every computation happens in the library's HIP kernels; there
+is no other code path, and a missing or unloadable library raises immediately.
 
-``attention_forward`` / ``attention_backward`` (and the varlen variants) are
-conveniences that allocate the outputs with torch and call the entry points.
+``attention_forward`` / ``attention_backward`` (and the varlen, decoding and
+FP8 variants) are conveniences that allocate the outputs (and workspaces) with
+torch and call the entry points.
 """
 
 from __future__ import annotations
