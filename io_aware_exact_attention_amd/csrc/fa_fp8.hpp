@@ -18,7 +18,8 @@
 // behaviour is never reached.
 //
 // Attention over the codes (fa_fwd_fp8_kernel): the bf16 forward's structure
-// with v_mfma_scale_f32_32x32x64_f8f6f4 (e4m3 x e4m3, unit block scales):
+// with v_mfma_scale_f32_32x32x64_f8f6f4 (e4m3 x e4m3; its e8m0 block-scale
+// operands are 2^0 except for the V tile's scale in O^T += V^T P^T):
 //   S^T = K Q^T: 64-deep k-steps over the head dim (2 per 32x32 block, d = 128);
 //   raw scores q8.k8 times c = scale*log2(e)/d * s_q(wave's block) * s_k(tile)
 //   give the base-2 exponent; the running max m is kept in those units;
