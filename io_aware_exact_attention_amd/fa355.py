@@ -93,6 +93,43 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+_BF16, _F32, _U8, _I32 = torch.bfloat16, torch.float32, torch.uint8, torch.int32
+
+
+class _Args:
+    """Checks of the tensors one call passes: what the C ABI cannot see through
+    a bare pointer -- the element type, a non-contiguous layout, a shape that
+    disagrees with the sizes passed -- and, once all of those hold, that every
+    tensor is in the memory of one GPU."""
+
+    def __init__(self):
+        self.seen = []
+
+    def need(self, name, t, dtype=None, shape=None, numel=None):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor")
+        if dtype is not None and t.dtype != dtype:
+            raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if shape is not None and tuple(t.shape) != tuple(int(x) for x in shape):
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+        if numel is not None and t.numel() != int(numel):
+            raise ValueError(f"{name} has {t.numel()} elements, expected {int(numel)}")
+        self.seen.append((name, t))
+        return self
+
+    def on_gpu(self):
+        dev = None
+        for name, t in self.seen:
+            if t.device.type != "cuda":
+                raise ValueError(f"{name} must be in GPU memory, got {t.device}")
+            if dev is None:
+                dev = t.device
+            elif t.device != dev:
+                raise ValueError(f"{name} is on {t.device}, the other tensors on {dev}")
+
+
 def _stream(stream):
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -106,14 +143,33 @@ def _dense_dims(q, k):
     return B, H, Nq, k.shape[1], d
 
 
-def fa_fwd(q, k, v, o, lse, scale: float, causal: bool, stream=None):
+def _check_dense(q, k, v, o=None, lse=None, extra=(), more=()):
+    """q [B,Nq,H,d], k and v [B,Nk,H,d] bf16, o like q, lse [B,H,Nq] fp32;
+    extra: (name, tensor, like) with like 'q' or 'k' for more bf16 tensors;
+    more: (name, tensor, dtype, shape) checked as given (shape None: any)."""
     B, H, Nq, Nk, d = _dense_dims(q, k)
+    a = _Args().need("q", q, _BF16)
+    a.need("k", k, _BF16, (B, Nk, H, d)).need("v", v, _BF16, (B, Nk, H, d))
+    if o is not None:
+        a.need("o", o, _BF16, (B, Nq, H, d))
+    if lse is not None:
+        a.need("lse", lse, _F32, (B, H, Nq))
+    for name, t, like in extra:
+        a.need(name, t, _BF16, (B, Nq, H, d) if like == "q" else (B, Nk, H, d))
+    for name, t, dtype, shape in more:
+        a.need(name, t, dtype, shape)
+    a.on_gpu()
+    return B, H, Nq, Nk, d
+
+
+def fa_fwd(q, k, v, o, lse, scale: float, causal: bool, stream=None):
+    B, H, Nq, Nk, d = _check_dense(q, k, v, o, lse)
     _check(lib().fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Nq, Nk, d,
                         float(scale), int(bool(causal)), _stream(stream)))
 
 
 def fa_fwd_persistent(q, k, v, o, lse, scale: float, causal: bool, stream=None):
-    B, H, Nq, Nk, d = _dense_dims(q, k)
+    B, H, Nq, Nk, d = _check_dense(q, k, v, o, lse)
     _check(lib().fa_fwd_persistent(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Nq, Nk, d,
                                    float(scale), int(bool(causal)), _stream(stream)))
 
@@ -123,7 +179,9 @@ def fa_bwd_workspace_bytes(batch_or_nseq: int, H: int, nq: int, d: int) -> int:
 
 
 def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, scale: float, causal: bool, stream=None):
-    B, H, Nq, Nk, d = _dense_dims(q, k)
+    B, H, Nq, Nk, d = _check_dense(q, k, v, o, lse,
+                                   (("dout", dout, "q"), ("dq", dq, "q"), ("dk", dk, "k"), ("dv", dv, "k")),
+                                   (("workspace", workspace, None, None),))
     nbytes = workspace.numel() * workspace.element_size()
     _check(lib().fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq),
                         _ptr(dk), _ptr(dv), _ptr(workspace), nbytes, B, H, Nq, Nk, d,
@@ -131,14 +189,19 @@ def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, scale: float, causal: b
 
 
 def fa_bwd_dot(o, dout, lse, workspace, stream=None):
+    if o.dim() != 4:
+        raise ValueError("dense tensors are [B, N, H, d]")
     B, Nq, H, d = o.shape
+    (_Args().need("o", o, _BF16).need("dout", dout, _BF16, o.shape).need("lse", lse, _F32, (B, H, Nq))
+     .need("workspace", workspace).on_gpu())
     nbytes = workspace.numel() * workspace.element_size()
     _check(lib().fa_bwd_dot(_ptr(o), _ptr(dout), _ptr(lse), _ptr(workspace), nbytes, B, H, Nq, d,
                             _stream(stream)))
 
 
 def fa_bwd_dkdv(q, k, v, dout, workspace, dk, dv, scale: float, causal: bool, stream=None):
-    B, H, Nq, Nk, d = _dense_dims(q, k)
+    B, H, Nq, Nk, d = _check_dense(q, k, v, extra=(("dout", dout, "q"), ("dk", dk, "k"), ("dv", dv, "k")),
+                                   more=(("workspace", workspace, None, None),))
     nbytes = workspace.numel() * workspace.element_size()
     _check(lib().fa_bwd_dkdv(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(workspace), nbytes,
                              _ptr(dk), _ptr(dv), B, H, Nq, Nk, d, float(scale),
@@ -146,16 +209,32 @@ def fa_bwd_dkdv(q, k, v, dout, workspace, dk, dv, scale: float, causal: bool, st
 
 
 def fa_bwd_dq(q, k, v, dout, workspace, dq, scale: float, causal: bool, stream=None):
-    B, H, Nq, Nk, d = _dense_dims(q, k)
+    B, H, Nq, Nk, d = _check_dense(q, k, v, extra=(("dout", dout, "q"), ("dq", dq, "q")),
+                                   more=(("workspace", workspace, None, None),))
     nbytes = workspace.numel() * workspace.element_size()
     _check(lib().fa_bwd_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(workspace), nbytes,
                            _ptr(dq), B, H, Nq, Nk, d, float(scale), int(bool(causal)),
                            _stream(stream)))
 
 
+def _check_packed(q, k, v, o, lse, cu_q, cu_k, max_q, extra=(), more=()):
+    if q.dim() != 3 or k.dim() != 3:
+        raise ValueError("packed tensors are [total, H, d]")
+    a = _Args().need("q", q, _BF16).need("cu_seqlens_q", cu_q, _I32)
+    nseq = cu_q.numel() - 1
+    a.need("cu_seqlens_k", cu_k, _I32, (nseq + 1,)).need("k", k, _BF16).need("v", v, _BF16, k.shape)
+    a.need("o", o, _BF16, q.shape).need("lse", lse, _F32, (nseq, q.shape[1], int(max_q)))
+    for name, t, like in extra:
+        a.need(name, t, _BF16, q.shape if like == "q" else k.shape)
+    for name, t, dtype, shape in more:
+        a.need(name, t, dtype, shape)
+    a.on_gpu()
+    return nseq
+
+
 def fa_fwd_varlen(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int,
                   max_seqlen_k: int, scale: float, causal: bool, stream=None):
-    nseq = cu_seqlens_q.numel() - 1
+    nseq = _check_packed(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, max_seqlen_q)
     _check(lib().fa_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(cu_seqlens_q),
                                _ptr(cu_seqlens_k), nseq, int(max_seqlen_q), int(max_seqlen_k),
                                q.shape[1], q.shape[2], float(scale), int(bool(causal)),
@@ -164,7 +243,9 @@ def fa_fwd_varlen(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int
 
 def fa_bwd_varlen(q, k, v, o, dout, lse, dq, dk, dv, workspace, cu_seqlens_q, cu_seqlens_k,
                   max_seqlen_q: int, max_seqlen_k: int, scale: float, causal: bool, stream=None):
-    nseq = cu_seqlens_q.numel() - 1
+    nseq = _check_packed(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
+                         (("dout", dout, "q"), ("dq", dq, "q"), ("dk", dk, "k"), ("dv", dv, "k")),
+                         (("workspace", workspace, None, None),))
     nbytes = workspace.numel() * workspace.element_size()
     _check(lib().fa_bwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse),
                                _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), nbytes,
@@ -179,8 +260,13 @@ def fa_decode_workspace_bytes(B: int, Hq: int, Hkv: int, Nq: int, Nk: int, d: in
 
 def fa_fwd_decode(q, k, v, o, lse, workspace, scale: float, causal: bool, stream=None):
     """q [B,Nq,Hq,d]; k, v [B,Nk,Hkv,d]; o like q; lse [B,Hq,Nq] fp32."""
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q [B,Nq,Hq,d]; k, v [B,Nk,Hkv,d]")
     B, Nq, Hq, d = q.shape
     Nk, Hkv = k.shape[1], k.shape[2]
+    (_Args().need("q", q, _BF16).need("k", k, _BF16, (B, Nk, Hkv, d)).need("v", v, _BF16, (B, Nk, Hkv, d))
+     .need("o", o, _BF16, q.shape).need("lse", lse, _F32, (B, Hq, Nq)).need("workspace", workspace)
+     .on_gpu())
     nbytes = workspace.numel() * workspace.element_size()
     _check(lib().fa_fwd_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(workspace),
                                nbytes, B, Hq, Hkv, Nq, Nk, d, float(scale), int(bool(causal)),
@@ -194,7 +280,10 @@ def fa_fp8_workspace_bytes(B: int, Nq: int, Nk: int, H: int, d: int) -> int:
 def fa_fwd_fp8(q, k, v, signs, o, lse, workspace, scale: float, causal: bool, rotate: bool = True,
                stream=None):
     """q [B,Nq,H,d]; k, v [B,Nk,H,d] bf16; signs fp32 [d]; o like q; lse [B,H,Nq] fp32."""
-    B, H, Nq, Nk, d = _dense_dims(q, k)
+    more = [("workspace", workspace, None, None)]
+    if rotate or signs is not None:
+        more.append(("signs", signs, _F32, (q.shape[-1],)))
+    B, H, Nq, Nk, d = _check_dense(q, k, v, o, lse, more=more)
     nbytes = workspace.numel() * workspace.element_size()
     _check(lib().fa_fwd_fp8(_ptr(q), _ptr(k), _ptr(v), _ptr(signs),
                             _ptr(o), _ptr(lse), _ptr(workspace), nbytes, B, Nq, Nk, H, d,
@@ -204,8 +293,15 @@ def fa_fwd_fp8(q, k, v, signs, o, lse, workspace, scale: float, causal: bool, ro
 def fa_fwd_fp8_codes(q8, k8, v8, sq, sk, sv, o, lse, qk_scale: float, causal: bool, stream=None):
     """q8 [B,Nq,H,d], k8, v8 [B,Nk,H,d] uint8 e4m3 codes; sq [B*H*ceil(Nq/64)], sk, sv
     [B*H*ceil(Nk/64)] fp32 power-of-two scales, one per 64-row block."""
+    if q8.dim() != 4 or k8.dim() != 4:
+        raise ValueError("codes are [B, N, H, d]")
     B, Nq, H, d = q8.shape
     Nk = k8.shape[1]
+    (_Args().need("q8", q8, _U8).need("k8", k8, _U8, (B, Nk, H, d)).need("v8", v8, _U8, (B, Nk, H, d))
+     .need("sq", sq, _F32, numel=B * H * ((Nq + 63) // 64))
+     .need("sk", sk, _F32, numel=B * H * ((Nk + 63) // 64))
+     .need("sv", sv, _F32, numel=B * H * ((Nk + 63) // 64))
+     .need("o", o, _BF16, (B, Nq, H, d)).need("lse", lse, _F32, (B, H, Nq)).on_gpu())
     _check(lib().fa_fwd_fp8_codes(_ptr(q8), _ptr(k8), _ptr(v8), _ptr(sq), _ptr(sk), _ptr(sv),
                                   _ptr(o), _ptr(lse), B, Nq, Nk, H, d, float(qk_scale),
                                   int(bool(causal)), _stream(stream)))
