@@ -34,8 +34,12 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: the HIP toolchain (ROCm) is required to build libfa355")
 
 
-def build(verbose: bool = False, extra_flags=None) -> str:
-    cmd = [hipcc(), *HIPCC_FLAGS, *(extra_flags or []), SRC, "-o", OUT + ".tmp"]
+# a C++ program that calls the library through the C ABI alone (host code; links libfa355.so)
+EXAMPLE_SRC = os.path.join(PKG_DIR, "csrc", "c_example.cpp")
+EXAMPLE_OUT = os.path.join(PKG_DIR, "fa355_c_example")
+
+
+def _run(cmd, verbose):
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError("hipcc failed:\n" + " ".join(cmd) + "\n" + res.stderr[-8000:])
@@ -44,7 +48,14 @@ def build(verbose: bool = False, extra_flags=None) -> str:
         for line in res.stderr.splitlines():
             if noise not in line:
                 print(line)
+
+
+def build(verbose: bool = False, extra_flags=None) -> str:
+    _run([hipcc(), *HIPCC_FLAGS, *(extra_flags or []), SRC, "-o", OUT + ".tmp"], verbose)
     os.replace(OUT + ".tmp", OUT)
+    _run([hipcc(), "-O2", "-std=c++17", EXAMPLE_SRC, "-o", EXAMPLE_OUT + ".tmp", "-L" + PKG_DIR,
+          "-lfa355", "-Wl,-rpath,$ORIGIN"], verbose)
+    os.replace(EXAMPLE_OUT + ".tmp", EXAMPLE_OUT)
     return OUT
 
 

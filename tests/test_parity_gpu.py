@@ -164,3 +164,30 @@ def test_stage_entry_points_match_fa_bwd():
     d_ref = (o.float() * do.float()).sum(-1).permute(0, 2, 1)       # [B, H, N]
     assert (nd + d_ref).abs().max().item() < 1e-4
     assert (l2 - lse * 1.4426950408889634).abs().max().item() < 1e-5
+
+
+def test_runs_on_the_callers_stream():
+    """Every entry point enqueues on the stream it is given: on a second stream
+    (default priority), ordered after the inputs' producer by an event, the
+    results equal the default stream's bit for bit."""
+    gu.need_gpu()
+    dev = torch.device("cuda", 0)
+    x = wl.make_dense(2, 300, 4, 128, seed=29)
+    q, k, v, do = (x[n].to(dev) for n in ("q", "k", "v", "dout"))
+    o1, l1 = fa355.attention_forward(q, k, v, 0.09, True)
+    g1 = fa355.attention_backward(q, k, v, o1, do, l1, 0.09, True)
+    side = torch.cuda.Stream(device=dev)
+    ready = torch.cuda.Event()
+    ready.record(torch.cuda.current_stream())
+    o2, l2 = torch.empty_like(o1), torch.empty_like(l1)
+    g2 = tuple(torch.empty_like(t) for t in (q, k, v))
+    ws = torch.empty(fa355.fa_bwd_workspace_bytes(2, 4, 300, 128) // 4, device=dev)
+    with torch.cuda.stream(side):
+        side.wait_event(ready)
+        fa355.fa_fwd(q, k, v, o2, l2, 0.09, True, stream=side)
+        fa355.fa_bwd(q, k, v, o2, do, l2, *g2, ws, 0.09, True, stream=side)
+    side.synchronize()
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    for a, b in zip(g1, g2):
+        assert torch.equal(a, b)
