@@ -182,9 +182,11 @@ int fa_fwd_decode(const void* q, const void* k, const void* v, void* o, float* l
  * dimensions before quantisation; V is quantised as it is.  Each block of 64
  * rows of each (batch, head) of each tensor gets one power-of-two scale
  * s = 2^ceil(log2(amax / 448)) and codes e4m3(x / s) (OCP E4M3, round to
- * nearest even).  The probabilities are quantised as e4m3(256 * exp(S - m)),
- * m the running maximum over 64-key tiles, for the P V product; the row sums
- * use the unrounded values.
+ * nearest even).  The probabilities are quantised as e4m3(16 * exp(S - m))
+ * for the P V product, m a per-row reference maximum that moves, over 64-key
+ * tiles, only when a tile's maximum exceeds it by more than ln 16 (the
+ * conditional rescale of "LLM Systems 22: Flash Attention", §4.2.1; so
+ * exp(S - m) <= 16); the row sums use the unrounded values.
  *   q [B,Nq,H,d], k, v [B,Nk,H,d], o [B,Nq,H,d] bf16; lse [B,H,Nq] fp32.
  *   d must be 128.  causal needs Nq == Nk.  Inputs must be finite.
  *   signs: device fp32 [d], each +1 or -1 (required when rotate = 1; ignored
@@ -207,7 +209,7 @@ int fa_fwd_fp8(const void* q, const void* k, const void* v, const float* signs, 
  * q8 [B,Nq,H,d], k8, v8 [B,Nk,H,d] (uint8, 16-byte aligned) and power-of-two
  * scales per 64-row block, sq [B*H][ceil(Nq/64)], sk, sv [B*H][ceil(Nk/64)]
  * fp32: S_ij = qk_scale * sq(i) * sk(j) * (q8_i . k8_j),
- * O_i = sum_j e4m3(256 P~_ij) sv(j) v8_j / (256 l_i).  d must be 128; scales
+ * O_i = sum_j e4m3(16 P~_ij) sv(j) v8_j / (16 l_i), P~ and l as above.  d must be 128; scales
  * that are not powers of two give unspecified results.
  */
 int fa_fwd_fp8_codes(const void* q8, const void* k8, const void* v8, const float* sq, const float* sk,

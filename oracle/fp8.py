@@ -32,12 +32,24 @@ Readings taken where the pages are silent (each one is a choice, stated):
   power of two is exact, so the code depends only on the value x.
 * Scores S_ij = scale * s_q(i) * s_k(j) / d * (q8_i . k8_j), decoded codes;
   V row j is s_v(j) * v8_j.
-* P~ = exp(S - m) lies in [0, 1]; the P V product uses p8 = e4m3(256 * P~)
-  and O = sum_j p8_j s_v(j) v8_j / (256 l), where l = sum_j P~_j is the
-  unquantised row sum; LSE = m + ln(l).  m is the online softmax's running
-  maximum over blocks of 64 keys ("08 · FlashAttention", §二), so P~ is rounded
-  relative to the maximum seen so far and earlier blocks are rescaled after
-  rounding: the one-pass kernel cannot know the final maximum when it rounds.
+* P~ = exp(S - m) with m a per-row reference maximum; the P V product uses
+  p8 = e4m3(2^(8 - tau) * P~) and O = sum_j p8_j s_v(j) v8_j / (2^(8 - tau) l),
+  where l = sum_j P~_j is the unquantised row sum; LSE = m + ln(l).  The keys
+  are visited in blocks of 64 ("08 · FlashAttention", §二), so P~ is rounded
+  relative to the reference at that block and earlier blocks are rescaled
+  after rounding: the one-pass kernel cannot know the final maximum when it
+  rounds.
+* The reference moves conditionally, the online-softmax variant of "LLM
+  Systems 22: Flash Attention", §4.2.1, which skips most rescaling (the page
+  gives no rule; read as a threshold): a block whose row maximum exceeds the
+  reference by more than tau * ln 2 (tau = 4: a factor 16) makes that maximum
+  the new reference and rescales the row's sums; otherwise the reference
+  stays, P~ <= 2^tau, and 2^(8 - tau) P~ <= 256 stays inside e4m3's range.
+  tau = 0 is the classic update (a new maximum always becomes the reference).
+  A decision within the tie window of the threshold may go either way in a
+  kernel's fp32 arithmetic and changes how later probabilities round, so such
+  a row's O is not unique: its slack is infinite (LSE does not depend on the
+  reference and keeps its bound).
 
 Layout: q, k, v [B, N, H, d]; codes the same, uint8; scales [B, H, nblk]; O
 [B, Nq, H, d]; LSE [B, H, Nq].
@@ -51,7 +63,7 @@ import torch
 
 _NEG_INF = float("-inf")
 E4M3_MAX = 448.0
-P_SCALE = 256.0          # P~ in [0, 1] is quantised as e4m3(256 * P~)
+RESCALE_LOG2 = 4.0       # tau: the reference maximum moves when exceeded by more than 2^tau
 KEY_BLOCK = 64           # keys per block of the online pass (the kernel's key tile)
 QUANT_ROWS = 64          # rows per quantisation scale
 
@@ -184,24 +196,31 @@ def row_scales(s: torch.Tensor, n: int, rows: int) -> torch.Tensor:
 def fp8_attention_forward(q8, k8, v8, sq, sk, sv, qk_scale: float, causal: bool,
                           tie_rel: float = 1e-5, q_scaled=None, k_scaled=None, v_scaled=None,
                           q_tie_atol=0.0, k_tie_atol=0.0, block: int | None = KEY_BLOCK,
-                          scale_rows: int = QUANT_ROWS):
+                          scale_rows: int = QUANT_ROWS, rescale_log2: float = RESCALE_LOG2,
+                          p_tie_rel: float | None = None):
     """Attention over decoded e4m3 codes with the P V product on e4m3 probabilities.
 
     q8 [B, Nq, H, d], k8/v8 [B, Nk, H, d] uint8 codes; sq, sk, sv [B, H, nblk]
     scales, one per block of ``scale_rows`` rows; S_ij = qk_scale * sq_i * sk_j *
     (q8_i . k8_j) and V row j is sv_j * v8_j.  The keys are visited in blocks of
-    ``block`` (None: one block) with the online softmax's running maximum m
-    ("08 · FlashAttention", §二): per block, P~ = exp(S - m_new) <= 1 is rounded
-    as e4m3(256 P~) for the P V product, earlier blocks' sums are rescaled by
-    e^(m - m_new), and the row sum l keeps the unrounded P~.  Rounding P~ at the
-    running maximum rather than the final one is what a one-pass kernel can do;
-    with one block the two agree.
+    ``block`` (None: one block) with the online softmax ("08 · FlashAttention",
+    §二) and a per-row reference maximum m: a block whose row maximum m_blk
+    exceeds m by more than rescale_log2 * ln 2 makes it the reference, and the
+    row's earlier sums are rescaled by e^(m - m_blk) ("LLM Systems 22: Flash
+    Attention", §4.2.1: most rescaling is skipped).  Per block P~ = exp(S - m)
+    <= 2^rescale_log2 is rounded as e4m3(2^(8 - rescale_log2) P~) for the P V
+    product, and the row sum l keeps the unrounded P~.  Rounding P~ at the
+    current reference rather than the final maximum is what a one-pass kernel
+    can do; with one block and rescale_log2 = 0 the two agree.
 
     Returns (O, LSE, slack_o, slack_lse): slack bounds, to first order, how far
     O and LSE may move when codes that sit at a near-tie (P~, and Q, K, V when
     their pre-rounding values q_scaled/k_scaled/v_scaled are given) round to the
     neighbouring code; a code counts as near a tie within max(tie_rel |x|,
-    *_tie_atol) of a midpoint.
+    *_tie_atol) of a midpoint (P codes: p_tie_rel |x|, default tie_rel).  A row with a reference decision within
+    tie_rel (|m| + |m_blk|) of the threshold gets slack_o = inf (either
+    decision is a correct execution, and they round later probabilities
+    differently).
     """
     qd, kd, vd = e4m3_decode(q8), e4m3_decode(k8), e4m3_decode(v8)
     B, Nq, H, d = qd.shape
@@ -216,6 +235,9 @@ def fp8_attention_forward(q8, k8, v8, sq, sk, sv, qk_scale: float, causal: bool,
     if Nk == 0:
         return o, lse, slack_o, slack_l
     bs = Nk if block is None else int(block)
+    p_scale = 2.0 ** (8.0 - rescale_log2)   # e4m3(p_scale * P~) <= 256
+    thr = rescale_log2 * math.log(2.0)
+    p_tie = tie_rel if p_tie_rel is None else p_tie_rel
 
     def tie_steps(scaled, codes, atol=0.0):
         if scaled is None:
@@ -248,32 +270,39 @@ def fp8_attention_forward(q8, k8, v8, sq, sk, sv, qk_scale: float, causal: bool,
             m = torch.full((Nq, 1), _NEG_INF, dtype=torch.float64)
             acc = torch.zeros(Nq, d, dtype=torch.float64)
             l = torch.zeros(Nq, 1, dtype=torch.float64)
-            tie_p = torch.zeros(Nq, d, dtype=torch.float64)   # P-tie steps * |v|, final units
-            tie_v = torch.zeros(Nq, d, dtype=torch.float64)   # p8 * V-tie steps, final units
+            # P-tie steps * |v| and p8 * V-tie steps, rescaled like acc (units of the
+            # current reference, which may stay below the row's true maximum)
+            tie_p = torch.zeros(Nq, d, dtype=torch.float64)
+            tie_v = torch.zeros(Nq, d, dtype=torch.float64)
+            amb = torch.zeros(Nq, 1, dtype=torch.bool)        # a reference decision at a near-tie
             for j0 in range(0, Nk, bs):
                 sb = s[:, j0:j0 + bs]
-                m_new = torch.maximum(m, sb.amax(dim=-1, keepdim=True))
+                m_blk = sb.amax(dim=-1, keepdim=True)
+                fin = (m > _NEG_INF) & (m_blk > _NEG_INF)
+                rise = torch.where(fin, m_blk - m, torch.zeros_like(m))
+                if thr > 0:   # with thr = 0 both choices give the same reference
+                    amb |= fin & ((rise - thr).abs() <= tie_rel * (m.abs() + m_blk.abs()))
+                m_new = torch.where(m_blk > m + thr, m_blk, m)          # the reference moves
                 m_ref = torch.where(m_new > _NEG_INF, m_new, torch.zeros_like(m_new))
                 alpha = torch.exp(m - m_ref)
-                pt = torch.exp(sb - m_ref)                            # P~ <= 1 at the running max
-                p8 = e4m3_encode(P_SCALE * pt)
+                pt = torch.exp(sb - m_ref)                            # P~ <= 2^tau
+                p8 = e4m3_encode(p_scale * pt)
                 pq = e4m3_decode(p8)
                 acc = alpha * acc + torch.matmul(pq, vh[j0:j0 + bs])
                 l = alpha * l + pt.sum(dim=-1, keepdim=True)
                 m = m_new
-                to_fin = torch.exp(m_ref - m_fin0)                   # later rescaling of this block
-                tp = e4m3_near_tie(P_SCALE * pt, tie_rel).to(torch.float64) * e4m3_step(p8)
-                tie_p += to_fin * torch.matmul(tp, vh[j0:j0 + bs].abs())
-                tie_v += to_fin * torch.matmul(pq, tvh[j0:j0 + bs])
+                tp = e4m3_near_tie(p_scale * pt, p_tie).to(torch.float64) * e4m3_step(p8)
+                tie_p = alpha * tie_p + torch.matmul(tp, vh[j0:j0 + bs].abs())
+                tie_v = alpha * tie_v + torch.matmul(pq, tvh[j0:j0 + bs])
             linv = torch.where(live, 1.0 / l, torch.zeros_like(l))
-            o[b, :, h] = acc / P_SCALE * linv
+            o[b, :, h] = acc / p_scale * linv
             lse[b, h] = torch.where(live, m + torch.log(l), torch.full_like(m, _NEG_INF)).squeeze(-1)
             # slack: P codes at a near-tie, V codes at a near-tie, and dS (first order)
             p_true = torch.exp(s - m_fin0) * torch.where(live, 1.0 / torch.exp(s - m_fin0).sum(-1, keepdim=True), torch.zeros_like(l))
             vabs = vh.abs()
-            so = (tie_p + tie_v) / P_SCALE * linv
+            so = (tie_p + tie_v) / p_scale * linv
             dev = torch.matmul(p_true * ds, vabs) + (p_true * ds).sum(-1, keepdim=True) * o[b, :, h].abs()
-            slack_o[b, :, h] = so + dev
+            slack_o[b, :, h] = torch.where(amb, torch.full_like(so, math.inf), so + dev)
             slack_l[b, h] = (p_true * ds).sum(dim=-1)
     return o, lse, slack_o, slack_l
 

@@ -150,10 +150,17 @@ def _exact_case(causal):
 
 
 def pin_fp8_attention_exact_powers_of_two(f):
-    # qk_scale = ln 2 and integer dot products in [-8, 8]: every P~ is 2^-k with
-    # k <= 16, so 256 P~ is an exact e4m3 value and nothing is lost
+    # qk_scale = ln 2 and integer dot products: every P~ is 2^-k, k the distance
+    # to the row's maximum (one block: the reference is the maximum), at most 10
+    # here, so 2^(8 - tau) P~ >= 2^-6 is an exact e4m3 value and nothing is lost
     for causal in (False, True):
         qv, kv, v8 = _exact_case(causal)
+        sc = torch.einsum("bihd,bjhd->bhij", qv, kv)
+        vis = torch.ones(19, 19, dtype=torch.bool)
+        if causal:
+            vis = vis.tril()
+        spread = sc.masked_fill(~vis, -99).amax(-1) - sc.masked_fill(~vis, 99).amin(-1)
+        assert spread.max().item() <= 10
         q8, k8 = f.e4m3_encode(qv), f.e4m3_encode(kv)
         ones = torch.ones(2, 2, dtype=torch.float64)
         for sv in (1.0, 0.25):
@@ -182,19 +189,79 @@ def pin_fp8_running_max_worked_example(f):
     k8 = enc(torch.tensor([[[[2.0, 0, 0, 0]], [[1.0, 0, 0, 0]], [[3.0, 0, 0, 0]]]], dtype=torch.float64))
     v8 = enc(torch.tensor([[[[1.0, 0, 0, 0]], [[3.0, 0, 0, 0]], [[4.0, 0, 0, 0]]]], dtype=torch.float64))
     one = torch.ones(1, 1, dtype=torch.float64)
-    o, lse, _, _ = f.fp8_attention_forward(q8, k8, v8, one, one, one, math.log(3.0), False, block=2)
+    o, lse, _, _ = f.fp8_attention_forward(q8, k8, v8, one, one, one, math.log(3.0), False, block=2,
+                                           rescale_log2=0.0)
     want = ((256 * 1 + 88 * 3) / 3 + 256 * 4) / (256 * 13 / 9)
     assert abs(o[0, 0, 0, 0].item() - want) < 1e-12, (o[0, 0, 0, 0].item(), want)
     assert abs(lse[0, 0, 0].item() - (3 * math.log(3.0) + math.log(13 / 9))) < 1e-12
     # one block: rounded at the final maximum
-    o1, _, _, _ = f.fp8_attention_forward(q8, k8, v8, one, one, one, math.log(3.0), False, block=None)
+    o1, _, _, _ = f.fp8_attention_forward(q8, k8, v8, one, one, one, math.log(3.0), False, block=None,
+                                          rescale_log2=0.0)
     assert abs(o1[0, 0, 0, 0].item() - (88 * 1 + 28 * 3 + 256 * 4) / (256 * 13 / 9)) < 1e-12
     assert d == q8.shape[-1]
 
 
+def _one_query_case(f, keys, values):
+    """q = e_0 and keys / values with only their first component set (exact codes)."""
+    enc = f.e4m3_encode
+    row = lambda x: [[x, 0.0, 0.0, 0.0]]
+    q8 = enc(torch.tensor([[row(1.0)]], dtype=torch.float64))
+    k8 = enc(torch.tensor([[row(float(x)) for x in keys]], dtype=torch.float64))
+    v8 = enc(torch.tensor([[row(float(x)) for x in values]], dtype=torch.float64))
+    return q8, k8, v8
+
+
+def pin_fp8_conditional_rescale_worked_example(f):
+    # one query, keys k = 2, 1, 3, 0, 5 with scores k ln 3, values 1, 3, 4, 2, 5, in
+    # blocks of 2; tau = 4, so the reference moves only on a rise above 4 ln 2 =
+    # 2.77 and P~ is rounded as e4m3(16 P~).
+    #   {0, 1}: reference 2 ln 3; P~ = 1, 1/3 -> 16, e4m3(5.33) = 5.5
+    #   {2, 3}: rise ln 3 = 1.10, kept; P~ = 3, 1/9 -> 48, e4m3(1.78) = 1.75
+    #   {4}:    rise 3 ln 3 = 3.30, moved; earlier sums x 1/27; P~ = 1 -> 16
+    # acc = (16 + 5.5*3 + 48*4 + 1.75*2) / 27 + 16*5 = 2388/27,
+    # l = (1 + 1/3 + 3 + 1/9) / 27 + 1 = 283/243, O_0 = acc / (16 l) = 21492/4528,
+    # LSE = ln(9 + 3 + 27 + 1 + 243) = ln 283.
+    # The classic update (tau = 0) gives 343854/72448 here; a threshold read in
+    # natural-log units (4 instead of 4 ln 2) keeps the reference at block {4}
+    # and gives 22212/4528.
+    q8, k8, v8 = _one_query_case(f, [2, 1, 3, 0, 5], [1, 3, 4, 2, 5])
+    one = torch.ones(1, 1, dtype=torch.float64)
+    c = math.log(3.0)
+    o, lse, so, sl = f.fp8_attention_forward(q8, k8, v8, one, one, one, c, False, block=2)
+    assert f.RESCALE_LOG2 == 4.0
+    assert abs(o[0, 0, 0, 0].item() - 21492 / 4528) < 1e-12, o[0, 0, 0, 0].item()
+    assert abs(lse[0, 0, 0].item() - math.log(283.0)) < 1e-12
+    assert bool(torch.isfinite(so).all())
+    o0, lse0, _, _ = f.fp8_attention_forward(q8, k8, v8, one, one, one, c, False, block=2, rescale_log2=0.0)
+    assert abs(o0[0, 0, 0, 0].item() - 343854 / 72448) < 1e-12, o0[0, 0, 0, 0].item()
+    assert abs(lse0[0, 0, 0].item() - math.log(283.0)) < 1e-12
+
+
+def pin_fp8_rescale_near_tie_flagged(f):
+    # scores 0 then 4 ln 2 (c = ln 2, keys 0 and 4), one key per block: the rise
+    # is exactly the threshold, either decision is a correct execution, so O has
+    # infinite slack; LSE = ln(1 + 16) either way.  A rise of 3 ln 2 is no tie.
+    one = torch.ones(1, 1, dtype=torch.float64)
+    c = math.log(2.0)
+    q8, k8, v8 = _one_query_case(f, [0, 4], [1, 2])
+    o, lse, so, sl = f.fp8_attention_forward(q8, k8, v8, one, one, one, c, False, block=1)
+    assert bool(torch.isinf(so[0, 0, 0]).all())
+    assert abs(lse[0, 0, 0].item() - math.log(17.0)) < 1e-12 and math.isfinite(sl[0, 0, 0].item())
+    # the two executions: keep (P~ = 16 -> code 256) or move (P~ = 1 -> 16, earlier
+    # sums / 16); both give O = (1 + 16 * 2) / 17 here, since every code is exact
+    assert abs(o[0, 0, 0, 0].item() - 33 / 17) < 1e-12
+    q8, k8, v8 = _one_query_case(f, [0, 3], [1, 2])
+    o, lse, so, _ = f.fp8_attention_forward(q8, k8, v8, one, one, one, c, False, block=1)
+    assert bool(torch.isfinite(so).all())
+    assert abs(o[0, 0, 0, 0].item() - 17 / 9) < 1e-12 and abs(lse[0, 0, 0].item() - math.log(9.0)) < 1e-12
+
+
 def pin_fp8_attention_p_rounding_bound(f):
     # random codes: the only difference from exact attention on the decoded inputs
-    # is rounding 256 P~ to e4m3: |dP~| <= max(P~ / 16, 2^-10 / 256)
+    # is rounding c P~ to e4m3, c = 2^(8 - tau): |dP~| <= max(P~ / 16, 2^-10 / c)
+    # (half a step: relative 2^-4 for normal codes, 2^-10 below 2^-6); every P~
+    # is scaled by e^(m_ref - m_final) <= 1 and the row sum is at least 1 in
+    # final units, so the error of O is at most sum_j (p_j / 16 + 2^-10 / c) |v_j|
     g = torch.Generator().manual_seed(408)
     B, N, H, d = 1, 40, 2, 16
     q8 = torch.randint(0, 255, (B, N, H, d), generator=g).to(torch.uint8)
@@ -210,18 +277,42 @@ def pin_fp8_attention_p_rounding_bound(f):
     def rows(sc):   # the scale of each row, [B, N, H, 1]
         return sc.repeat_interleave(16, dim=2)[:, :, :N].transpose(1, 2)[..., None]
 
-    for causal in (False, True):
-        o, lse, _, _ = f.fp8_attention_forward(q8, k8, v8, sq, sk, sv, 0.37, causal, scale_rows=16)
+    for causal, tau in ((False, 0.0), (True, 0.0), (False, f.RESCALE_LOG2), (True, f.RESCALE_LOG2)):
+        o, lse, _, _ = f.fp8_attention_forward(q8, k8, v8, sq, sk, sv, 0.37, causal, scale_rows=16,
+                                               block=8, rescale_log2=tau)
         qd = f.e4m3_decode(q8) * rows(sq)
         kd = f.e4m3_decode(k8) * rows(sk)
         vd = f.e4m3_decode(v8) * rows(sv)
         o_ref, lse_ref = dense.attention_forward(qd, kd, vd, 0.37, causal)
         p = dense.attention_probs(qd, kd, 0.37, causal)            # [B, H, N, N]
-        bound = torch.einsum("bhij,bjhd->bihd", p / 16 + 2.0 ** -18, vd.abs())
+        bound = torch.einsum("bhij,bjhd->bihd", p / 16 + 2.0 ** -10 / 2.0 ** (8 - tau), vd.abs())
         diff = (o - o_ref).abs()
-        assert bool((diff <= bound * (1 + 1e-9) + 1e-13).all()), causal
+        assert bool((diff <= bound * (1 + 1e-9) + 1e-13).all()), (causal, tau)
         assert diff.max().item() > 1e-6                            # P~ is rounded
         assert (lse - lse_ref).abs().max().item() < 1e-10
+
+
+def pin_fp8_slack_covers_p_rounding(f):
+    # with every P code counted as near a tie (p_tie_rel = 1) and exact Q, K, V,
+    # slack_o is sum_j step(p8_j) |v_j| in the row's final units, which bounds
+    # the effect of rounding P: |O - O_exact| <= slack_o + sum_j 2^-10 / c |v_j|
+    # (c = 2^(8 - tau); the second term: subnormal codes, rounded by less than
+    # 2^-10 / c but too small to count as near a tie).  Random codes in blocks
+    # of 8 keys give rows whose reference stays below the true maximum.
+    g = torch.Generator().manual_seed(413)
+    B, N, H, d = 1, 96, 2, 16
+    q8, k8, v8 = (torch.randint(0, 255, (B, N, H, d), generator=g).to(torch.uint8) for _ in range(3))
+    for t in (q8, k8, v8):
+        t[(t & 127) >= 0x70] = 0x30                    # no NaN codes, magnitudes below 2^7
+    ones = torch.ones(B, H, 2, dtype=torch.float64)
+    qd, kd, vd = f.e4m3_decode(q8), f.e4m3_decode(k8), f.e4m3_decode(v8)
+    for causal in (False, True):
+        o, lse, so, _ = f.fp8_attention_forward(q8, k8, v8, ones, ones, ones, 2e-4, causal, p_tie_rel=1.0,
+                                                block=8)
+        assert bool(torch.isfinite(so).all())
+        o_ref, _ = dense.attention_forward(qd, kd, vd, 2e-4, causal)
+        tol = 2.0 ** -10 / 2.0 ** (8 - f.RESCALE_LOG2) * vd.abs().sum(dim=1, keepdim=True)
+        assert bool(((o - o_ref).abs() <= so * (1 + 1e-9) + tol + 1e-13).all()), causal
 
 
 def pin_fp8_forward_close_and_rotation_helps(f):
@@ -251,6 +342,9 @@ ALL_PINS = [
     pin_quantize_scale_and_codes,
     pin_fp8_attention_exact_powers_of_two,
     pin_fp8_running_max_worked_example,
+    pin_fp8_conditional_rescale_worked_example,
+    pin_fp8_rescale_near_tie_flagged,
     pin_fp8_attention_p_rounding_bound,
+    pin_fp8_slack_covers_p_rounding,
     pin_fp8_forward_close_and_rotation_helps,
 ]

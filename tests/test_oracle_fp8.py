@@ -41,13 +41,25 @@ MUTATIONS = {
                              "return s.repeat_interleave(int(rows), dim=2)[:, :, 1:n + 1] if s.shape[2] * int(rows) > n else s.repeat_interleave(int(rows), dim=2)[:, :, :n]"),
     "quantise_per_head": ("rows = N if block_rows is None else int(block_rows)\n    nblk",
                           "rows = N\n    nblk"),
-    "p_scale_not_undone": ("o[b, :, h] = acc / P_SCALE * linv", "o[b, :, h] = acc * linv"),
+    "p_scale_not_undone": ("o[b, :, h] = acc / p_scale * linv", "o[b, :, h] = acc * linv"),
     "v_scale_dropped": ("vh = vd[b, :, h] * rv[b, h][:, None]", "vh = vd[b, :, h]"),
-    "p_not_quantised": ("p8 = e4m3_encode(P_SCALE * pt)\n                pq = e4m3_decode(p8)",
-                        "p8 = e4m3_encode(P_SCALE * pt)\n                pq = P_SCALE * pt"),
-    "p_rounded_at_final_max": ("p8 = e4m3_encode(P_SCALE * pt)\n                pq = e4m3_decode(p8)",
-                               "p8 = e4m3_encode(P_SCALE * torch.exp(sb - m_fin0))\n"
+    "p_not_quantised": ("p8 = e4m3_encode(p_scale * pt)\n                pq = e4m3_decode(p8)",
+                        "p8 = e4m3_encode(p_scale * pt)\n                pq = p_scale * pt"),
+    "p_rounded_at_final_max": ("p8 = e4m3_encode(p_scale * pt)\n                pq = e4m3_decode(p8)",
+                               "p8 = e4m3_encode(p_scale * torch.exp(sb - m_fin0))\n"
                                "                pq = e4m3_decode(p8) * torch.exp(m_fin0 - m_ref)"),
+    "p_scale_fixed_256": ("p_scale = 2.0 ** (8.0 - rescale_log2)", "p_scale = 256.0"),
+    "rescale_always": ("m_new = torch.where(m_blk > m + thr, m_blk, m)", "m_new = torch.maximum(m, m_blk)"),
+    "threshold_natural_units": ("thr = rescale_log2 * math.log(2.0)", "thr = rescale_log2"),
+    "threshold_not_strict_sign": ("m_new = torch.where(m_blk > m + thr, m_blk, m)",
+                                  "m_new = torch.where(m_blk > m - thr, m_blk, m)"),
+    "alpha_from_block_max": ("alpha = torch.exp(m - m_ref)", "alpha = torch.exp(m - torch.maximum(m_ref, m_blk))"),
+    "slack_at_true_maximum": ("tie_p = alpha * tie_p + torch.matmul(tp, vh[j0:j0 + bs].abs())",
+                              "tie_p = alpha * tie_p + torch.exp(m_ref - m_fin0) * torch.matmul(tp, vh[j0:j0 + bs].abs())"),
+    "near_tie_not_flagged": ("amb |= fin & ((rise - thr).abs() <= tie_rel * (m.abs() + m_blk.abs()))",
+                             "amb |= fin & ((rise - thr).abs() < 0.0)"),
+    "near_tie_flags_everything": ("amb |= fin & ((rise - thr).abs() <= tie_rel * (m.abs() + m_blk.abs()))",
+                                  "amb |= fin"),
     "acc_not_rescaled": ("acc = alpha * acc + torch.matmul(pq, vh[j0:j0 + bs])",
                          "acc = acc + torch.matmul(pq, vh[j0:j0 + bs])"),
     "sum_not_rescaled": ("l = alpha * l + pt.sum(dim=-1, keepdim=True)",
