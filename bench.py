@@ -1,8 +1,9 @@
 """Benchmark: exact attention forward + backward on one MI355X.
 
 One step = the whole hot path on the headline workload (B8 H16 N4096 d128,
-causal, bf16): fa_fwd, then the backward's three stages (fa_bwd_dot,
-fa_bwd_dkdv, fa_bwd_dq), all on one stream with inputs resident in HBM.
+causal, bf16): fa_fwd, then the backward's two stages as fa_bwd runs them
+(fa_bwd_dq_dot: dQ with the row-dot D folded in; then fa_bwd_dkdv), all on one
+stream with inputs resident in HBM.
 W untimed warm-up steps, then exactly K timed steps bracketed by device
 synchronisation; HIP events around each kernel give per-kernel durations.
 
@@ -479,14 +480,13 @@ def main():
     scale = w.scale
 
     persistent = args.forward == "persistent"
-    names = ["fa_fwd_persistent_kernel" if persistent else "fa_fwd_kernel", "fa_bwd_dot_kernel",
-             "fa_bwd_dkdv_kernel", "fa_bwd_dq_kernel"]
+    names = ["fa_fwd_persistent_kernel" if persistent else "fa_fwd_kernel", "fa_bwd_dq_kernel",
+             "fa_bwd_dkdv_kernel"]
     fwd = fa355.fa_fwd_persistent if persistent else fa355.fa_fwd
-    calls = [
+    calls = [   # fa_bwd = fa_bwd_dq_dot, then fa_bwd_dkdv (one kernel each)
         lambda: fwd(q, k, v, o, lse, scale, causal),
-        lambda: fa355.fa_bwd_dot(o, do, lse, ws),
+        lambda: fa355.fa_bwd_dq_dot(q, k, v, o, do, lse, ws, dq, scale, causal),
         lambda: fa355.fa_bwd_dkdv(q, k, v, do, ws, dk, dv, scale, causal),
-        lambda: fa355.fa_bwd_dq(q, k, v, do, ws, dq, scale, causal),
     ]
     calibration_copy(dev)
 
@@ -513,33 +513,24 @@ def main():
     cnt = acc.dense_counts(B, H, N, d, causal)
     pairs = cnt["pairs"]
     f_fwd, f_bwd = cnt["flops_fwd"], cnt["flops_bwd"]
-    # algorithmic FLOPs / bytes attributed per kernel (the 10d backward = 8d in dK/dV + 2d in dQ)
-    kern_flops = [f_fwd, 0, 8 * d * pairs, 2 * d * pairs]
-    dot_bytes = B * N * H * (2 * 2 * d + 4 + 8)   # O, dO, LSE in; -D, LSE*log2(e) out
+    # algorithmic FLOPs attributed per kernel (the 10d backward = 2d in dQ + 8d in dK/dV)
+    kern_flops = [f_fwd, 2 * d * pairs, 8 * d * pairs]
     kern = {}
     for n, ms, fl, ts in zip(names, kern_ms, kern_flops, per_step):
         ts = sorted(ts)
-        e = {"ms": round(ms, 4), "ms_median": round(ts[len(ts) // 2], 4), "ms_min": round(ts[0], 4)}
-        if fl:
-            e["tflops"] = round(fl / (ms * 1e-3) / 1e12, 2)
-        else:
-            e["gbs"] = round(dot_bytes / (ms * 1e-3) / 1e9, 1)
-        kern[n] = e
-    # algorithmic HBM bytes per launch (each input read once, each output written once)
+        kern[n] = {"ms": round(ms, 4), "ms_median": round(ts[len(ts) // 2], 4), "ms_min": round(ts[0], 4),
+                   "tflops": round(fl / (ms * 1e-3) / 1e12, 2)}
+    # algorithmic HBM bytes per launch (each input read once, each output written once):
+    # dQ + row-dot reads q, k, v, o, dout, LSE and writes dq, -D, LSE*log2(e);
+    # dK/dV reads q, k, v, dout, -D, LSE*log2(e) and writes dk, dv
     tok = B * N * H
-    kern_bytes = [cnt["bytes_fwd"], dot_bytes, tok * (2 * 4 * d + 8) + tok * 2 * 2 * d,
-                  tok * (2 * 4 * d + 8) + tok * 2 * d]
+    kern_bytes = [cnt["bytes_fwd"], tok * (5 * 2 * d + 4) + tok * (2 * d + 8),
+                  tok * (4 * 2 * d + 8) + tok * 2 * 2 * d]
     traffic = measured_traffic(w.name)
     dom = max(range(len(names)), key=lambda i: kern_ms[i])
-    if kern_flops[dom]:
-        achieved = kern_flops[dom] / (kern_ms[dom] * 1e-3) / 1e12
-        roof = {"kernel": names[dom], "bound": "mfma", "achieved": round(achieved, 2),
-                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_BF16_TFLOPS, 4)}
-    else:
-        achieved = dot_bytes / (kern_ms[dom] * 1e-3) / 1e9
-        roof = {"kernel": names[dom], "bound": "hbm", "achieved": round(achieved, 1),
-                "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4)}
+    achieved = kern_flops[dom] / (kern_ms[dom] * 1e-3) / 1e12
+    roof = {"kernel": names[dom], "bound": "mfma", "achieved": round(achieved, 2),
+            "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4)}
     roof["traffic"] = traffic.get(names[dom]) if traffic else None
     roof["algorithmic_bytes"] = kern_bytes[dom]
     for n, b_alg in zip(names, kern_bytes):

@@ -124,17 +124,23 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
            int causal, void* stream);
 
 /*
- * The three stages fa_bwd runs, exposed separately (dense batch only) for callers
- * that time them or need only some gradients.  Arguments mean what they mean in
+ * The backward's stages, exposed separately (dense batch only) for callers that
+ * time them or need only some gradients.  Arguments mean what they mean in
  * fa_bwd; `workspace` is fa_bwd's workspace (fa_bwd_workspace_bytes(B,H,Nq,d)
  * bytes, 4-byte aligned).
- *   fa_bwd_dot:  fills the workspace: -D_i (D_i = sum_c dO_ic * O_ic) and
- *                LSE_i * log2(e), from o, dout and lse
- *   fa_bwd_dkdv: dK, dV from q, k, v, dout and the workspace   (writes dk, dv)
- *   fa_bwd_dq:   dQ from q, k, v, dout and the workspace       (writes dq)
- * fa_bwd_dkdv and fa_bwd_dq both need the workspace that fa_bwd_dot filled on the
- * same stream.  Errors as fa_bwd.
+ *   fa_bwd_dq_dot: dQ, and fills the workspace as fa_bwd_dot does, from q, k,
+ *                  v, o, dout and lse                          (writes dq)
+ *   fa_bwd_dot:    fills the workspace: -D_i (D_i = sum_c dO_ic * O_ic) and
+ *                  LSE_i * log2(e), from o, dout and lse
+ *   fa_bwd_dkdv:   dK, dV from q, k, v, dout and the workspace (writes dk, dv)
+ *   fa_bwd_dq:     dQ from q, k, v, dout and the workspace     (writes dq)
+ * fa_bwd is fa_bwd_dq_dot then fa_bwd_dkdv.  fa_bwd_dkdv and fa_bwd_dq need a
+ * workspace that fa_bwd_dq_dot or fa_bwd_dot filled on the same stream; both fill
+ * it with the same values bit for bit.  Errors as fa_bwd.
  */
+int fa_bwd_dq_dot(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                  const float* lse, void* workspace, size_t workspace_bytes, void* dq, int B,
+                  int H, int Nq, int Nk, int d, float scale, int causal, void* stream);
 int fa_bwd_dot(const void* o, const void* dout, const float* lse, void* workspace,
                size_t workspace_bytes, int B, int H, int Nq, int d, void* stream);
 int fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout,

@@ -114,28 +114,36 @@ int launch_bwd_dkdv_d(AttnParams p, int causal, hipStream_t s) {
                   : launch(fa_bwd_dkdv_kernel<D, false, VARLEN>, grid, KV::NW * 64, s, p);
 }
 
-template <int D, bool VARLEN>
+template <int D, bool VARLEN, bool DOT>
 int launch_bwd_dq_d(AttnParams p, int causal, hipStream_t s) {
     using Q = BwdQCfg<D>;
     p.n_tiles = (p.nq + Q::BM - 1) / Q::BM;
     const int grid = p.n_tiles * p.H * p.batch;
-    return causal ? launch(fa_bwd_dq_kernel<D, true, VARLEN>, grid, Q::NW * 64, s, p)
-                  : launch(fa_bwd_dq_kernel<D, false, VARLEN>, grid, Q::NW * 64, s, p);
+    return causal ? launch(fa_bwd_dq_kernel<D, true, VARLEN, DOT>, grid, Q::NW * 64, s, p)
+                  : launch(fa_bwd_dq_kernel<D, false, VARLEN, DOT>, grid, Q::NW * 64, s, p);
 }
 
-enum BwdStage { kStageDot = 1, kStageDkdv = 2, kStageDq = 4, kStageAll = 7 };
+// The whole backward is kStageDqDot (the dQ kernel with the row-dot folded in:
+// it writes -D and LSE * log2(e) as well as dQ), then dK/dV.  The row-dot kernel
+// alone (kStageDot) fills the same workspace for the stand-alone dK/dV and dQ
+// stages.  Stages run in this order: dQ + row-dot, row-dot, dK/dV, dQ.
+enum BwdStage { kStageDot = 1, kStageDkdv = 2, kStageDq = 4, kStageDqDot = 8,
+                kStageAll = kStageDqDot | kStageDkdv };
 
 template <bool VARLEN>
 int launch_bwd(const AttnParams& p, int d, int causal, hipStream_t s, int stages = kStageAll) {
     int st = FA_OK;
-    if (stages & kStageDot)
+    if (stages & kStageDqDot)
+        st = d == 64 ? launch_bwd_dq_d<64, VARLEN, true>(p, causal, s)
+                     : launch_bwd_dq_d<128, VARLEN, true>(p, causal, s);
+    if (!st && (stages & kStageDot))
         st = d == 64 ? launch_bwd_dot_d<64, VARLEN>(p, s) : launch_bwd_dot_d<128, VARLEN>(p, s);
     if (!st && (stages & kStageDkdv))
         st = d == 64 ? launch_bwd_dkdv_d<64, VARLEN>(p, causal, s)
                      : launch_bwd_dkdv_d<128, VARLEN>(p, causal, s);
     if (!st && (stages & kStageDq))
-        st = d == 64 ? launch_bwd_dq_d<64, VARLEN>(p, causal, s)
-                     : launch_bwd_dq_d<128, VARLEN>(p, causal, s);
+        st = d == 64 ? launch_bwd_dq_d<64, VARLEN, false>(p, causal, s)
+                     : launch_bwd_dq_d<128, VARLEN, false>(p, causal, s);
     return st;
 }
 
@@ -317,6 +325,29 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
     p.dv = static_cast<bf16*>(dv);
     set_workspace(p, workspace);
     return launch_bwd<false>(p, d, causal, static_cast<hipStream_t>(stream));
+}
+
+int fa_bwd_dq_dot(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                  const float* lse, void* workspace, size_t workspace_bytes, void* dq, int B, int H,
+                  int Nq, int Nk, int d, float scale, int causal, void* stream) {
+    if (!q || !k || !v || !o || !dout || !lse || !dq) return FA_ERR_NULL;
+    if (B <= 0 || Nq <= 0 || Nk <= 0) return FA_ERR_SHAPE;
+    int st = check_common(H, d, scale, causal);
+    if (st) return st;
+    if (causal && Nq != Nk) return FA_ERR_UNSUPPORTED;
+    if (!workspace || workspace_bytes < fa_bwd_workspace_bytes(B, H, Nq, d)) return FA_ERR_WORKSPACE;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(dout, 16) ||
+        !aligned(dq, 16) || !aligned(lse, 4) || !aligned(workspace, 4))
+        return FA_ERR_ALIGN;
+    st = check_sizes((int64_t)B * Nq, (int64_t)B * Nk, Nq, Nk, H, d, (int64_t)((Nq + 15) / 16) * H * B);
+    if (st) return st;
+    AttnParams p = base_params(q, k, v, B, H, Nq, Nk, scale);
+    p.o_in = static_cast<const bf16*>(o);
+    p.dout = static_cast<const bf16*>(dout);
+    p.lse_in = lse;
+    p.dq = static_cast<bf16*>(dq);
+    set_workspace(p, workspace);
+    return launch_bwd<false>(p, d, causal, static_cast<hipStream_t>(stream), kStageDqDot);
 }
 
 int fa_bwd_dot(const void* o, const void* dout, const float* lse, void* workspace,

@@ -11,7 +11,10 @@
 // is owned by exactly one work-group, so results are bitwise deterministic):
 //   1. fa_bwd_dot_kernel:  D_i = rowsum(dO * O), one pass over O and dO; it
 //      stores -D_i and LSE_i * log2(e), the forms the other two kernels consume
-//      (-D seeds the dP accumulator, so dP - D costs no arithmetic).
+//      (-D seeds the dP accumulator, so dP - D costs no arithmetic).  The whole
+//      backward runs it inside the dQ kernel instead (kernel 3 with DOT: each
+//      query row's dO is already in that kernel's registers), which then runs
+//      first; the separate kernel serves the stage-by-stage entry points.
 //   2. fa_bwd_dkdv_kernel: key-tile outer.  A work-group owns a 128-key tile
 //      (K rows in registers, 32 keys per wave; V in LDS) and keeps the dK^T,
 //      dV^T accumulators on chip, streams the query rows that can see those keys
@@ -289,8 +292,11 @@ void fa_bwd_dkdv_kernel(AttnParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// 3. dQ (query-tile outer)
-template <int D, bool CAUSAL, bool VARLEN>
+// 3. dQ (query-tile outer).  With DOT it first computes D_i = rowsum(dO * O) of
+// its own rows (kernel 1's products, summed in kernel 1's pairwise order, so the
+// values are bitwise the same) and stores -D_i and LSE_i * log2(e) for the dK/dV
+// kernel, which must then run after it.
+template <int D, bool CAUSAL, bool VARLEN, bool DOT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fa_bwd_dq_kernel(AttnParams p) {
     using C = BwdQCfg<D>;
@@ -331,8 +337,36 @@ void fa_bwd_dq_kernel(AttnParams p) {
         }
     }
     const int64_t srow = ((int64_t)b * p.H + h) * p.nq + qrow;
-    const float lse2 = p.lse2[srow];   // LSE * log2(e)
-    const float nd = p.dvec[srow];     // -D
+    float lse2, nd;   // LSE * log2(e), -D
+    if constexpr (DOT) {
+        // this lane holds 16-byte chunks 2s + h2 (s < KSTEPS) of its row; kernel 1
+        // gives each chunk one thread, an fma chain over its 8 products, then a
+        // butterfly over chunk distances TPR/2, ..., 2, 1: here distances 2w are
+        // the in-lane pairs (s, s + w) and distance 1 is the other half-wave
+        const bf16* optr = p.o_in + (int64_t)(qs + qrow) * tok + h * D + 8 * h2;
+        float a[C::KSTEPS];
+#pragma unroll
+        for (int st = 0; st < C::KSTEPS; ++st) {
+            const bf16x8 of = load16(optr + 16 * st);
+            float acc = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc = __builtin_fmaf((float)of[e], (float)gf[st][e], acc);
+            a[st] = acc;
+        }
+#pragma unroll
+        for (int w = C::KSTEPS / 2; w > 0; w >>= 1)
+#pragma unroll
+            for (int st = 0; st < w; ++st) a[st] += a[st + w];
+        nd = -sum_halves(a[0]);
+        lse2 = p.lse_in[srow] * kLog2e;
+        if (h2 == 0 && qi < nq) {
+            p.dvec[srow] = nd;
+            p.lse2[srow] = lse2;
+        }
+    } else {
+        lse2 = p.lse2[srow];
+        nd = p.dvec[srow];
+    }
     const float c = p.scale_log2;
 
     f32x16 acc[C::DBLK];

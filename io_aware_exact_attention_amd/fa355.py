@@ -1,7 +1,8 @@
 """Python binding of libfa355 (ctypes).  Argument marshalling only.
 
 The functions named like the C entry points (``fa_fwd``, ``fa_fwd_persistent``,
-``fa_bwd`` and its stages ``fa_bwd_dot`` / ``fa_bwd_dkdv`` / ``fa_bwd_dq``,
+``fa_bwd`` and its stages ``fa_bwd_dq_dot`` / ``fa_bwd_dot`` / ``fa_bwd_dkdv`` /
+``fa_bwd_dq``,
 ``fa_fwd_varlen``, ``fa_bwd_varlen``, ``fa_fwd_decode``, ``fa_fwd_fp8``,
 ``fa_fwd_fp8_codes``, the ``*_workspace_bytes`` queries, ``fa_status_string``)
 take torch tensors that already live on the GPU, pass their device pointers and
@@ -39,6 +40,7 @@ _SIGNATURES = {
     "fa_bwd_dot": (_c_int, [_vp] * 4 + [_sz] + [_c_int] * 4 + [_vp]),
     "fa_bwd_dkdv": (_c_int, [_vp] * 5 + [_sz] + [_vp] * 2 + [_c_int] * 5 + [_c_float, _c_int, _vp]),
     "fa_bwd_dq": (_c_int, [_vp] * 5 + [_sz] + [_vp] + [_c_int] * 5 + [_c_float, _c_int, _vp]),
+    "fa_bwd_dq_dot": (_c_int, [_vp] * 7 + [_sz] + [_vp] + [_c_int] * 5 + [_c_float, _c_int, _vp]),
     "fa_decode_workspace_bytes": (_sz, [_c_int] * 6),
     "fa_fwd_decode": (_c_int, [_vp] * 6 + [_sz] + [_c_int] * 6 + [_c_float, _c_int, _vp]),
     "fa_fp8_workspace_bytes": (_sz, [_c_int] * 5),
@@ -186,6 +188,15 @@ def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, scale: float, causal: b
     _check(lib().fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq),
                         _ptr(dk), _ptr(dv), _ptr(workspace), nbytes, B, H, Nq, Nk, d,
                         float(scale), int(bool(causal)), _stream(stream)))
+
+
+def fa_bwd_dq_dot(q, k, v, o, dout, lse, workspace, dq, scale: float, causal: bool, stream=None):
+    B, H, Nq, Nk, d = _check_dense(q, k, v, o, lse, extra=(("dout", dout, "q"), ("dq", dq, "q")),
+                                   more=(("workspace", workspace, None, None),))
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(lib().fa_bwd_dq_dot(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse),
+                               _ptr(workspace), nbytes, _ptr(dq), B, H, Nq, Nk, d, float(scale),
+                               int(bool(causal)), _stream(stream)))
 
 
 def fa_bwd_dot(o, dout, lse, workspace, stream=None):

@@ -110,6 +110,15 @@ def test_stage_entry_points_reject():
     assert lib.fa_bwd_dq(*[A] * 4, A, W, MIS, 1, 1, 16, 16, 64, 0.1, 0, None) == -4
     assert lib.fa_bwd_dq(*[A] * 4, A, W, A, 1, 1, 0, 16, 64, 0.1, 0, None) == -2
 
+    def dqdot(q=A, o=A, lse=A, ws=A, wsb=W, dq=A, B=1, H=1, Nq=16, Nk=16, d=64, scale=0.1, causal=0):
+        return lib.fa_bwd_dq_dot(q, A, A, o, A, lse, ws, wsb, dq, B, H, Nq, Nk, d, scale, causal, None)
+
+    assert dqdot(q=None) == -1 and dqdot(o=None) == -1 and dqdot(lse=None) == -1 and dqdot(dq=None) == -1
+    assert dqdot(Nq=0) == -2 and dqdot(B=0) == -2
+    assert dqdot(d=72) == -3 and dqdot(Nk=8, causal=1) == -3 and dqdot(scale=0.0) == -3
+    assert dqdot(dq=MIS) == -4 and dqdot(o=MIS) == -4
+    assert dqdot(ws=None) == -6 and dqdot(wsb=2 * 4 * 16 - 1) == -6
+
 
 def test_decode_rejects():
     lib = fa355.lib()

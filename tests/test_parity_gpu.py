@@ -143,23 +143,31 @@ def test_outputs_fully_overwritten():
         assert torch.isfinite(t).all()
 
 
-def test_stage_entry_points_match_fa_bwd():
-    """fa_bwd_dot, fa_bwd_dkdv and fa_bwd_dq run the kernels fa_bwd runs: the same
-    gradients bit for bit, and the workspace holds -D and LSE*log2(e)."""
+@pytest.mark.parametrize("d", [64, 128])
+def test_stage_entry_points_match_fa_bwd(d):
+    """fa_bwd is fa_bwd_dq_dot then fa_bwd_dkdv; fa_bwd_dot fills the workspace
+    with the same values bit for bit as fa_bwd_dq_dot, so fa_bwd_dot, fa_bwd_dkdv
+    and fa_bwd_dq give the same gradients bit for bit too; the workspace holds -D
+    and LSE*log2(e)."""
     gu.need_gpu()
     dev = torch.device("cuda", 0)
-    x = wl.make_dense(2, 200, 3, 128, seed=23)
+    gu.announce(f"backward stages d={d}")
+    x = wl.make_dense(2, 200, 3, d, seed=23)
     q, k, v, do = (x[n].to(dev) for n in ("q", "k", "v", "dout"))
     o, lse = fa355.attention_forward(q, k, v, 0.1, True)
     ref = fa355.attention_backward(q, k, v, o, do, lse, 0.1, True)
-    ws = torch.empty(fa355.fa_bwd_workspace_bytes(2, 3, 200, 128) // 4, device=dev)
-    dq, dk, dv = (torch.full_like(t, float("nan")) for t in (q, k, v))
+    nws = fa355.fa_bwd_workspace_bytes(2, 3, 200, d) // 4
+    ws, ws2 = (torch.full((nws,), float("nan"), device=dev) for _ in range(2))
+    dq, dk, dv, dq2, dk2, dv2 = (torch.full_like(t, float("nan")) for t in (q, k, v) * 2)
     fa355.fa_bwd_dot(o, do, lse, ws)
     fa355.fa_bwd_dkdv(q, k, v, do, ws, dk, dv, 0.1, True)
     fa355.fa_bwd_dq(q, k, v, do, ws, dq, 0.1, True)
+    fa355.fa_bwd_dq_dot(q, k, v, o, do, lse, ws2, dq2, 0.1, True)
+    fa355.fa_bwd_dkdv(q, k, v, do, ws2, dk2, dv2, 0.1, True)
     torch.cuda.synchronize()
-    for a, b in zip((dq, dk, dv), ref):
-        assert torch.equal(a, b)
+    assert torch.equal(ws, ws2)
+    for a, a2, b in zip((dq, dk, dv), (dq2, dk2, dv2), ref):
+        assert torch.equal(a, b) and torch.equal(a2, b)
     nd, l2 = ws.view(2, 2, 3, 200)
     d_ref = (o.float() * do.float()).sum(-1).permute(0, 2, 1)       # [B, H, N]
     assert (nd + d_ref).abs().max().item() < 1e-4
