@@ -30,6 +30,8 @@
 // accumulating dQ across key tiles with atomics.
 #pragma once
 
+#include <type_traits>
+
 #include "fa_tiles.hpp"
 
 namespace fa355 {
@@ -192,16 +194,19 @@ void fa_bwd_dkdv_kernel(AttnParams p) {
     };
 
     if (n_q > 0) issue(0);
-    for (int it = 0; it < n_q; ++it) {
-        const FA_LDS char* qt = lds + C::STAGE0 + (it & 1) * 2 * C::TILE_BYTES;
+    // one query stage, two per trip of the loop below (constant LDS buffer offsets,
+    // as in the forward)
+    auto step = [&](int it, auto buf) __attribute__((always_inline)) {
+        constexpr int SB = decltype(buf)::value;   // this stage's buffer
+        const FA_LDS char* qt = lds + C::STAGE0 + SB * 2 * C::TILE_BYTES;
         const FA_LDS char* gt = qt + C::TILE_BYTES;
-        const FA_LDS float* lse_t = (const FA_LDS float*)(lds + C::STATS0 + (it & 1) * C::STAT_BYTES);
+        const FA_LDS float* lse_t = (const FA_LDS float*)(lds + C::STATS0 + SB * C::STAT_BYTES);
         const FA_LDS float* nd_t = lse_t + 64;
         wait_vmem();
         __syncthreads();
         if (it + 1 < n_q) issue(it + 1);
         const int q0 = q_first + it * C::BMQ;
-        if (CAUSAL && q0 + 31 < kw0) continue;   // every query here precedes every key
+        if (CAUSAL && q0 + 31 < kw0) return;   // every query here precedes every key
 
         // S = Q K^T and dP - D = dO V^T - D: rows are queries (this lane's rows are
         // q0 + 8*(r/4) + 4*h2 + r%4), columns this wave's keys.  The dP
@@ -273,6 +278,10 @@ void fa_bwd_dkdv_kernel(AttnParams p) {
                 dka[cb] = mfma_32x32x16(aq, db[kk], dka[cb]);
             }
         }
+    };
+    for (int it = 0; it < n_q; it += 2) {   // two stages per trip: buffer offsets are constants
+        step(it, std::integral_constant<int, 0>{});
+        if (it + 1 < n_q) step(it + 1, std::integral_constant<int, 1>{});
     }
 
     if (key < nk) {
@@ -384,18 +393,21 @@ void fa_bwd_dq_kernel(AttnParams p) {
         loader.load(lds, kbase, kv_bytes, 0, wave_s);
         loader.load(lds + C::TILE_BYTES, vbase, kv_bytes, 0, wave_s);
     }
-    for (int t = 0; t < n_kv; ++t) {
-        const FA_LDS char* kt = lds + (t & 1) * 2 * C::TILE_BYTES;
+    // one key tile, two per trip of the loop below (constant LDS buffer offsets, as
+    // in the forward)
+    auto step = [&](int t, auto buf) __attribute__((always_inline)) {
+        constexpr int B0 = decltype(buf)::value * 2 * C::TILE_BYTES;        // this tile's buffer
+        constexpr int B1 = (1 - decltype(buf)::value) * 2 * C::TILE_BYTES;  // the next tile's
+        const FA_LDS char* kt = lds + B0;
         const FA_LDS char* vt = kt + C::TILE_BYTES;
         wait_vmem();
         __syncthreads();
         if (t + 1 < n_kv) {
-            FA_LDS char* kn = lds + ((t + 1) & 1) * 2 * C::TILE_BYTES;
-            loader.load(kn, kbase, kv_bytes, (t + 1) * C::BN * row_bytes, wave_s);
-            loader.load(kn + C::TILE_BYTES, vbase, kv_bytes, (t + 1) * C::BN * row_bytes, wave_s);
+            loader.load(lds + B1, kbase, kv_bytes, (t + 1) * C::BN * row_bytes, wave_s);
+            loader.load(lds + B1 + C::TILE_BYTES, vbase, kv_bytes, (t + 1) * C::BN * row_bytes, wave_s);
         }
         const int kv0 = t * C::BN;
-        if (CAUSAL && kv0 > qw0 + 31) continue;
+        if (CAUSAL && kv0 > qw0 + 31) return;
 
         // S^T = K Q^T, dP^T = V dO^T: rows keys, columns this wave's queries
         f32x16 sT[C::KB], dpT[C::KB];
@@ -451,6 +463,10 @@ void fa_bwd_dq_kernel(AttnParams p) {
                 acc[cb] = mfma_32x32x16(a, dsk[k2], acc[cb]);
             }
         }
+    };
+    for (int t = 0; t < n_kv; t += 2) {   // two tiles per trip: buffer offsets are constants
+        step(t, std::integral_constant<int, 0>{});
+        if (t + 1 < n_kv) step(t + 1, std::integral_constant<int, 1>{});
     }
 
     if (qi < nq) {

@@ -27,6 +27,8 @@
 //     row-wise K reads and the transposed V reads are free of bank conflicts.
 #pragma once
 
+#include <type_traits>
+
 #include "fa_tiles.hpp"
 
 namespace fa355 {
@@ -92,18 +94,26 @@ __device__ __forceinline__ void fwd_tile(const AttnParams& p, char* smem, int bh
         loader.load(ldsb, kbase, kv_bytes, 0, wave_s);
         loader.load(ldsb + C::TILE_BYTES, vbase, kv_bytes, 0, wave_s);
     }
-    for (int t = 0; t < n_kv; ++t) {
-        char* kt = smem + (t & 1) * 2 * C::TILE_BYTES;
-        char* vt = kt + C::TILE_BYTES;
+    // per-lane byte offsets of the K operand reads (one per k-step) within a tile
+    int koff[C::KSTEPS];
+#pragma unroll
+    for (int st = 0; st < C::KSTEPS; ++st) koff[st] = tile_off<D>(col, 2 * st + h2);
+    // One key tile.  The loop below runs two per trip, so that each tile's LDS
+    // buffer is a compile-time constant: it goes into the LDS reads' immediate
+    // offsets instead of costing vector adds per operand read (2-3% measured).
+    auto step = [&](int t, auto buf) __attribute__((always_inline)) {
+        constexpr int KB0 = decltype(buf)::value * 2 * C::TILE_BYTES;   // this tile's buffer
+        constexpr int KB1 = (1 - decltype(buf)::value) * 2 * C::TILE_BYTES;
+        const FA_LDS char* kt = ldsb + KB0;
+        const FA_LDS char* vt = kt + C::TILE_BYTES;
         wait_vmem();
         __syncthreads();
         if (t + 1 < n_kv) {
-            FA_LDS char* kn = ldsb + ((t + 1) & 1) * 2 * C::TILE_BYTES;
-            loader.load(kn, kbase, kv_bytes, (t + 1) * C::BN * row_bytes, wave_s);
-            loader.load(kn + C::TILE_BYTES, vbase, kv_bytes, (t + 1) * C::BN * row_bytes, wave_s);
+            loader.load(ldsb + KB1, kbase, kv_bytes, (t + 1) * C::BN * row_bytes, wave_s);
+            loader.load(ldsb + KB1 + C::TILE_BYTES, vbase, kv_bytes, (t + 1) * C::BN * row_bytes, wave_s);
         }
         const int kv0 = t * C::BN;
-        if (CAUSAL && kv0 > qw0 + 31) continue;   // every key here is above this wave's rows
+        if (CAUSAL && kv0 > qw0 + 31) return;   // every key here is above this wave's rows
 
         // S^T[key][query] = K Q^T for the tile's 64 keys
         f32x16 s[C::KB];
@@ -111,10 +121,10 @@ __device__ __forceinline__ void fwd_tile(const AttnParams& p, char* smem, int bh
         for (int kb = 0; kb < C::KB; ++kb) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
-            const int row = kb * 32 + col;
 #pragma unroll
             for (int st = 0; st < C::KSTEPS; ++st) {
-                bf16x8 a = lds_read16((const FA_LDS char*)(kt + tile_off<D>(row, 2 * st + h2)));
+                // row kb*32 + col: 32 more rows keep the swizzle
+                bf16x8 a = lds_read16(kt + koff[st] + kb * 32 * C::ROW_BYTES);
                 s[kb] = mfma_32x32x16(a, qf[st], s[kb]);
             }
         }
@@ -180,11 +190,15 @@ __device__ __forceinline__ void fwd_tile(const AttnParams& p, char* smem, int bh
             for (int cb = 0; cb < C::DBLK; ++cb) {
                 const int c0 = cb * 32 + 16 * g;
                 const int rk = ks2 * 16 * C::ROW_BYTES;   // 16 more rows keep the swizzle
-                bf16x8 a = join(lds_read_tr((const FA_LDS char*)(vt + tr_off<D>(4 * h2, c0, sl) + rk)),
-                                lds_read_tr((const FA_LDS char*)(vt + tr_off<D>(4 * h2 + 8, c0, sl) + rk)));
+                bf16x8 a = join(lds_read_tr(vt + tr_off<D>(4 * h2, c0, sl) + rk),
+                                lds_read_tr(vt + tr_off<D>(4 * h2 + 8, c0, sl) + rk));
                 acc[cb] = mfma_32x32x16(a, pk[ks2], acc[cb]);
             }
         }
+    };
+    for (int t = 0; t < n_kv; t += 2) {
+        step(t, std::integral_constant<int, 0>{});
+        if (t + 1 < n_kv) step(t + 1, std::integral_constant<int, 1>{});
     }
 
     const float lt = sum_halves(l);
