@@ -42,6 +42,8 @@
 // 2t + i / 8, t = 0..7 (8 rows of one column).
 #pragma once
 
+#include <type_traits>
+
 #include "fa_tiles.hpp"
 
 namespace fa355 {
@@ -348,8 +350,14 @@ void fa_fwd_fp8_kernel(Fp8AttnParams p) {
     // the next tile's K/V loads
     float sk_next = n_kv > 0 ? skh[0] : 1.f;
     float sv_next = n_kv > 0 ? svh[0] : 1.f;
-    for (int t = 0; t < n_kv; ++t) {
-        const FA_LDS char* kt = ldsb + (t & 1) * 2 * C::TILE_BYTES;
+    // One key tile in LDS buffer `buf` (0 or 1).  The causal kernel runs two tiles
+    // per trip with `buf` a compile-time constant, carried in the LDS reads'
+    // immediate offsets instead of vector adds (5% faster); the non-causal kernel,
+    // which would spill at three waves per SIMD that way, passes it at run time.
+    auto step = [&](int t, auto buf) __attribute__((always_inline)) {
+        const int B0 = int(buf) * 2 * C::TILE_BYTES;         // this tile's buffer
+        const int B1 = (1 - int(buf)) * 2 * C::TILE_BYTES;   // the next tile's
+        const FA_LDS char* kt = ldsb + B0;
         const FA_LDS char* vt = kt + C::TILE_BYTES;
         wait_vmem();
         __syncthreads();
@@ -357,12 +365,11 @@ void fa_fwd_fp8_kernel(Fp8AttnParams p) {
         if (t + 1 < n_kv) {
             sk_next = skh[t + 1];
             sv_next = svh[t + 1];
-            FA_LDS char* kn = ldsb + ((t + 1) & 1) * 2 * C::TILE_BYTES;
-            loader.load(kn, kbase, kv_bytes, (t + 1) * C::BN * row_bytes, wave_s);
-            loader.load(kn + C::TILE_BYTES, vbase, kv_bytes, (t + 1) * C::BN * row_bytes, wave_s);
+            loader.load(ldsb + B1, kbase, kv_bytes, (t + 1) * C::BN * row_bytes, wave_s);
+            loader.load(ldsb + B1 + C::TILE_BYTES, vbase, kv_bytes, (t + 1) * C::BN * row_bytes, wave_s);
         }
         const int kv0 = t * C::BN;
-        if (CAUSAL && kv0 > qw0 + 31) continue;
+        if (CAUSAL && kv0 > qw0 + 31) return;
         const float c = c0 * sk_t;
         const int ev = 127 + __builtin_amdgcn_frexp_expf(sv_t) - 1;   // s_v = 2^(ev - 127)
 
@@ -446,6 +453,14 @@ void fa_fwd_fp8_kernel(Fp8AttnParams p) {
             acc[cb] = mfma_fp8_32x32x64_scale_a(__builtin_shufflevector(a01, a23, 0, 1, 2, 3, 4, 5, 6, 7), pk,
                                                 acc[cb], ev);
         }
+    };
+    if constexpr (CAUSAL) {
+        for (int t = 0; t < n_kv; t += 2) {
+            step(t, std::integral_constant<int, 0>{});
+            if (t + 1 < n_kv) step(t + 1, std::integral_constant<int, 1>{});
+        }
+    } else {
+        for (int t = 0; t < n_kv; ++t) step(t, t & 1);
     }
 
     const float lt = sum_halves(l);
