@@ -118,15 +118,31 @@ __device__ __forceinline__ void fwd_tile(const AttnParams& p, char* smem, int bh
         // S^T[key][query] = K Q^T for the tile's 64 keys
         f32x16 s[C::KB];
 #pragma unroll
-        for (int kb = 0; kb < C::KB; ++kb) {
+        for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+        bf16x8 ka[C::KSTEPS][C::KB];
 #pragma unroll
-            for (int st = 0; st < C::KSTEPS; ++st) {
+        for (int st = 0; st < C::KSTEPS; ++st)
+#pragma unroll
+            for (int kb = 0; kb < C::KB; ++kb)
                 // row kb*32 + col: 32 more rows keep the swizzle
-                bf16x8 a = lds_read16(kt + koff[st] + kb * 32 * C::ROW_BYTES);
-                s[kb] = mfma_32x32x16(a, qf[st], s[kb]);
+                ka[st][kb] = lds_read16(kt + koff[st] + kb * 32 * C::ROW_BYTES);
+#pragma unroll
+        for (int st = 0; st < C::KSTEPS; ++st)
+#pragma unroll
+            for (int kb = 0; kb < C::KB; ++kb)
+                s[kb] = mfma_32x32x16(ka[st][kb], qf[st], s[kb]);
+        {   // keep AHEAD operand reads in flight ahead of the products (as compiled,
+            // each product otherwise waited for its own read: 1.3% on the forward)
+            constexpr int NR = C::KSTEPS * C::KB, AHEAD = 6;
+            __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);
+#pragma unroll
+            for (int i = 0; i < NR - AHEAD; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
             }
+            __builtin_amdgcn_sched_group_barrier(0x008, AHEAD, 0);
         }
 
         // causal diagonal / ragged tail
