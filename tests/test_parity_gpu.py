@@ -199,3 +199,41 @@ def test_runs_on_the_callers_stream():
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
     for a, b in zip(g1, g2):
         assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+def test_rows_past_a_sequence_read_as_zeros(d, causal):
+    """Tiles that run past a sequence's last row must not see the next one's rows:
+    the kernels' buffer resources end at the sequence, so those rows read as zeros.
+    Here every row after the first sequence is NaN; if any of it reached the first
+    sequence's products (0 * NaN = NaN), its outputs would not be finite."""
+    gu.need_gpu()
+    gu.announce(f"NaN neighbours d={d} causal={causal}")
+    dev = torch.device("cuda", 0)
+    scale = d ** -0.5
+    # dense: batch entry 1 follows batch entry 0 in memory
+    x = wl.make_dense(2, 77, 2, d, seed=400 + d)
+    xn = {n: t.clone() for n, t in x.items()}
+    for t in xn.values():
+        t[1] = float("nan")
+    g = gu.run_dense(xn, scale, causal)
+    ref = gu.oracle_dense({n: t[:1] for n, t in x.items()}, scale, causal)
+    gu.check_forward(g["o"][:1], g["lse"][:1].cpu(), ref["o"], ref["lse"], "dense batch 0")
+    gu.check_grads([t[:1] for t in g["grads"]], ref["grads"], "dense batch 0")
+    # varlen: sequence 1 (130 rows of NaN) follows sequence 0 (77 rows)
+    lens = [77, 130]
+    xp = wl.make_packed(lens, 2, d, seed=500 + d)
+    cu = xp["cu_seqlens"]
+    q, k, v, do = (xp[n].clone() for n in ("q", "k", "v", "dout"))
+    for t in (q, k, v, do):
+        t[77:] = float("nan")
+    qd, kd, vd, dod, cud = (t.to(dev) for t in (q, k, v, do, cu))
+    o, lse = fa355.attention_forward_varlen(qd, kd, vd, cud, cud, max(lens), max(lens), scale, causal)
+    grads = fa355.attention_backward_varlen(qd, kd, vd, o, dod, lse, cud, cud, max(lens), max(lens),
+                                            scale, causal)
+    torch.cuda.synchronize()
+    s0 = {"q": q[None, :77], "k": k[None, :77], "v": v[None, :77], "dout": do[None, :77]}
+    r0 = gu.oracle_dense(s0, scale, causal)
+    gu.check_forward(o[None, :77], lse[:1, :, :77].cpu(), r0["o"], r0["lse"], "varlen sequence 0")
+    gu.check_grads([t[None, :77] for t in grads], r0["grads"], "varlen sequence 0")
