@@ -68,3 +68,21 @@ def test_decode_workload_full_size():
         o_ref, lse_ref = oracle.decode_forward(xs["q"], xs["k"], xs["v"], scale, w.causal)
         gu.check_forward(o[b:b + 1, :, hs], lse[b:b + 1, hs], o_ref, lse_ref,
                          f"decode workload b={b} kv head {hkv}")
+
+
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+def test_cache_rows_past_a_sequence_read_as_zeros(causal):
+    """The last key chunk of sequence 0 runs past its 700 cached rows into sequence
+    1's cache, which here is all NaN: those rows must read as zeros."""
+    gu.need_gpu()
+    gu.announce(f"decode NaN neighbours causal={causal}")
+    dev = torch.device("cuda", 0)
+    scale = 128 ** -0.5
+    y = wl.make_decode(2, 4, 700, 8, 2, 128, seed=2100)
+    yn = {n: t.clone() for n, t in y.items()}
+    for t in yn.values():
+        t[1] = float("nan")
+    o, lse = fa355.attention_decode(*(yn[n].to(dev) for n in ("q", "k", "v")), scale, causal)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.decode_forward(y["q"][:1], y["k"][:1], y["v"][:1], scale, causal)
+    gu.check_forward(o[:1], lse[:1].cpu(), o_ref, lse_ref, "decode sequence 0")

@@ -227,3 +227,20 @@ def test_fp8_workload_full_size_sampled():
             x["q"][b:b + 1, :, sl_], x["k"][b:b + 1, :, sl_], x["v"][b:b + 1, :, sl_], x["signs"],
             base.scale, True, True, TIE_REL, fp32_rotation=True)
         _check(o[b:b + 1, :, sl_], lse[b:b + 1, sl_], o_ref, lse_ref, so, sl, f"full size b{b} h{h}")
+
+
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+def test_fp8_rows_past_a_sequence_read_as_zeros(causal):
+    """Batch entry 1 is all NaN (its quantisation scales and codes are NaN); the
+    tiles of batch entry 0 that run past its 77 rows must read zeros, not those."""
+    gu.need_gpu()
+    gu.announce(f"fp8 NaN neighbours causal={causal}")
+    x = _inputs(2, 77, 77, 2, seed=3900)
+    xn = {n: (t.clone() if n != "signs" else t) for n, t in x.items()}
+    for n in ("q", "k", "v"):
+        xn[n][1] = float("nan")
+    scale = 128 ** -0.5
+    o, lse, _ = _run_full(xn, scale, causal)
+    o_ref, lse_ref, so, sl, _, _ = of8.fp8_forward(x["q"][:1], x["k"][:1], x["v"][:1], x["signs"], scale,
+                                                   causal, True, TIE_REL, fp32_rotation=True)
+    _check(o[:1], lse[:1], o_ref, lse_ref, so, sl, "fp8 batch 0 with NaN neighbours")
