@@ -17,7 +17,9 @@ CASES = [
     (1, 300, 300, 3, 64, True),        # B*H not a multiple of 8, ragged tail
     (2, 129, 257, 5, 128, False),
     (1, 64, 64, 1, 64, True),          # fewer items than work-groups
-    (4, 2048, 2048, 16, 128, True),
+    (4, 2048, 2048, 16, 128, True),    # two full rounds of the deal (the second reversed)
+    (3, 2048, 2048, 16, 128, True),    # 768 items: a partial reversed round
+    (1, 4096, 4096, 20, 128, True),    # 640 items, 20 pairs (not a multiple of 8)
 ]
 
 
