@@ -31,14 +31,18 @@ struct AttnParams {
 };
 
 // Token range of batch entry / sequence b: rows [q0, q0+nq) of q, [k0, k0+nk) of k.
+// A packed sequence's lengths are clamped to [0, max_seqlen]: offsets that break
+// the documented precondition (a sequence longer than max_seqlen, decreasing
+// offsets) then leave rows uncomputed instead of indexing past the
+// [nseq, H, max_seqlen_q] planes of lse and the backward workspace.
 template <bool VARLEN>
 __device__ __forceinline__ void seq_range(const AttnParams& p, int b, int& q0, int& nq,
                                           int& k0, int& nk) {
     if constexpr (VARLEN) {
         q0 = p.cu_q[b];
-        nq = p.cu_q[b + 1] - q0;
+        nq = min(max(p.cu_q[b + 1] - q0, 0), p.nq);
         k0 = p.cu_k[b];
-        nk = p.cu_k[b + 1] - k0;
+        nk = min(max(p.cu_k[b + 1] - k0, 0), p.nk);
     } else {
         q0 = b * p.nq;
         nq = p.nq;
