@@ -237,3 +237,50 @@ def test_rows_past_a_sequence_read_as_zeros(d, causal):
     r0 = gu.oracle_dense(s0, scale, causal)
     gu.check_forward(o[None, :77], lse[:1, :, :77].cpu(), r0["o"], r0["lse"], "varlen sequence 0")
     gu.check_grads([t[None, :77] for t in grads], r0["grads"], "varlen sequence 0")
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_understated_max_seqlen_stays_in_bounds(causal):
+    """A sequence longer than max_seqlen breaks the documented precondition.  The
+    kernels clamp each sequence to max_seqlen rows, so nothing outside the
+    [nseq, H, max_seqlen] planes of lse and the workspace is written (guard
+    regions around both stay NaN), the well-formed sequences still match the
+    oracle, and the long one's first max_seqlen rows (causal: they see only keys
+    below max_seqlen) match it too."""
+    gu.need_gpu()
+    lens, H, d, mx = [100, 300, 50], 2, 128, 200
+    gu.announce(f"varlen lengths {lens} with max_seqlen {mx} (understated), causal={causal}")
+    scale = d ** -0.5
+    x = wl.make_packed(lens, H, d, seed=4242)
+    dev = torch.device("cuda", 0)
+    q, k, v, do = (x[n].to(dev) for n in ("q", "k", "v", "dout"))
+    cu = x["cu_seqlens"].to(dev)
+    nseq = len(lens)
+    guard = 4096
+    plane = nseq * H * mx
+    lse_buf = torch.full((guard + plane + guard,), float("nan"), dtype=torch.float32, device=dev)
+    lse = lse_buf[guard:guard + plane].view(nseq, H, mx)
+    ws_n = fa355.fa_bwd_workspace_bytes(nseq, H, mx, d) // 4
+    ws_buf = torch.full((guard + ws_n + guard,), float("nan"), dtype=torch.float32, device=dev)
+    ws = ws_buf[guard:guard + ws_n]
+    o = torch.full_like(q, float("nan"))
+    fa355.fa_fwd_varlen(q, k, v, o, lse, cu, cu, mx, mx, scale, causal)
+    dq, dk, dv = (torch.full_like(t, float("nan")) for t in (q, k, v))
+    fa355.fa_bwd_varlen(q, k, v, o, do, lse, dq, dk, dv, ws, cu, cu, mx, mx, scale, causal)
+    torch.cuda.synchronize()
+    for buf in (lse_buf, ws_buf):
+        assert torch.isnan(buf[:guard]).all() and torch.isnan(buf[-guard:]).all()
+    cu_h = x["cu_seqlens"].tolist()
+    for s in range(nseq):
+        a, e = cu_h[s], cu_h[s + 1]
+        n = min(e - a, mx)
+        if e - a > mx and not causal:
+            continue   # the clamped key range changes every row of the long sequence
+        xs = {nm: x[nm][None, a:e].contiguous() for nm in ("q", "k", "v", "dout")}
+        r = gu.oracle_dense(xs, scale, causal, backward=(e - a <= mx))
+        gu.check_forward(o[None, a:a + n], lse[s:s + 1, :, :n], r["o"][:, :n], r["lse"][..., :n],
+                         f"sequence {s}")
+        if e - a <= mx:
+            gu.check_grads((dq[None, a:e], dk[None, a:e], dv[None, a:e]), r["grads"], f"sequence {s}")
+        else:
+            assert torch.isnan(o[a + mx:e]).all()   # rows past max_seqlen are not computed
