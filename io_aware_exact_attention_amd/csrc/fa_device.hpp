@@ -73,6 +73,26 @@ __device__ __forceinline__ bf16x8 pack8(const float* f) {
     return __builtin_bit_cast(bf16x8, u);
 }
 
+// acc + the two bf16 values packed in `pair` (v_dot2_f32_bf16 against (1, 1): the
+// products are exact, so this adds two bf16 values in fp32).  Written as inline
+// assembly: the ROCm 7.2 compiler lowers __builtin_amdgcn_fdot2_f32_bf16 on the
+// dwords of a 4-dword vector to v_dot2c_f32_bf16 instructions that all read the
+// vector's first dword (seen in the generated code).  The VOP3P form names its
+// source register explicitly.
+__device__ __forceinline__ float add2_bf16(uint32_t pair, float acc) {
+    float r;
+    asm("v_dot2_f32_bf16 %0, %1, %2, %3" : "=v"(r) : "v"(pair), "s"(0x3f803f80u), "v"(acc));
+    return r;
+}
+
+// acc + the sum of the 8 bf16 values of p.
+__device__ __forceinline__ float sum8_bf16(bf16x8 p, float acc) {
+    const u32x4 u = __builtin_bit_cast(u32x4, p);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc = add2_bf16(u[j], acc);
+    return acc;
+}
+
 __device__ __forceinline__ bf16x8 load16(const bf16* p) {
     return *reinterpret_cast<const bf16x8*>(p);
 }

@@ -6,7 +6,9 @@
 // unnormalised accumulator O; a new tile with scores S' updates them as
 //     m_new = max(m, rowmax S'),  P~ = exp(S' - m_new),
 //     l <- e^(m - m_new) l + rowsum P~,   O <- e^(m - m_new) O + P~ V',
-// and O / l is written once at the end with LSE = m + ln l.  Work is done in the
+// and O / l is written once at the end with LSE = m + ln l.  (Here P~ is rounded
+// to bf16 for the P V product; O is divided by the sum of those rounded values,
+// LSE uses the unrounded l.)  Work is done in the
 // base-2 domain: exp(x*scale) = exp2(x * scale*log2 e), the scale folded into
 // one FMA per score.  With the causal mask only key tiles at or below the
 // diagonal are visited, and only tiles that straddle it are masked.
@@ -87,7 +89,8 @@ __device__ __forceinline__ void fwd_tile(const AttnParams& p, char* smem, int bh
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[cb][r] = 0.f;
     float m = kNegInf;   // running max of raw scores q.k (this row)
-    float l = 0.f;       // running sum, over the keys this lane holds
+    float l = 0.f;       // running sum, over the keys this lane holds (gives LSE)
+    float lr = 0.f;      // the same sum of the bf16-rounded P~ that the P V product uses
     const float c = p.scale_log2;
 
     if (n_kv > 0) {
@@ -195,6 +198,13 @@ __device__ __forceinline__ void fwd_tile(const AttnParams& p, char* smem, int bh
             for (int e = 0; e < 8; ++e) tmp[e] = s[ks2 >> 1][8 * (ks2 & 1) + e];
             pk[ks2] = pack8(tmp);
         }
+        // O is normalised by the sum of the probabilities it was formed from:
+        // O = sum_j bf16(P~_j) v_j / sum_j bf16(P~_j) is a convex combination of
+        // the v_j, whose error from P's rounding scales with v_j - O rather than v_j
+        float rr = lr * alpha;
+#pragma unroll
+        for (int ks2 = 0; ks2 < C::BN / 16; ++ks2) rr = sum8_bf16(pk[ks2], rr);
+        lr = rr;
 
         // O^T[dim][query] += V^T P^T; V^T operand via transposed LDS reads of the
         // same key order: rows 16*ks + 4*h2 + 0..3 and +8.
@@ -218,7 +228,8 @@ __device__ __forceinline__ void fwd_tile(const AttnParams& p, char* smem, int bh
     }
 
     const float lt = sum_halves(l);
-    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    const float lrt = sum_halves(lr);
+    const float inv = lrt > 0.f ? 1.f / lrt : 0.f;
     if (qi < nq) {
         bf16* optr = p.o + (int64_t)(qs + qi) * tok + h * D;
 #pragma unroll
