@@ -40,11 +40,36 @@ def max_abs(a, b) -> float:
     return (f64(a) - f64(b)).abs().max().item() if a.numel() else 0.0
 
 
+def bf16_ulp(x):
+    """Spacing of bf16 values at |x| (8 significant bits): 2^(floor(log2|x|) - 7)."""
+    a = f64(x).abs().clamp(min=2.0 ** -126)
+    return torch.ldexp(torch.ones_like(a), torch.floor(torch.log2(a)) - 7)
+
+
 def check_forward(o_gpu, lse_gpu, o_ref, lse_ref, what=""):
+    """O max-abs <= O_TOL and LSE max-abs <= LSE_TOL.
+
+    Output floor (the reading of the O tolerance for bf16 outputs): an entry
+    whose own rounding floor |bf16(O_ref) - O_ref| is already >= O_TOL (possible
+    only for |O_ref| >= 4, where bf16 values are 2^-5 apart) cannot meet O_TOL in
+    any bf16 output.  Such entries are reported as a spec floor, not counted as
+    a pass of O_TOL, and held to one bf16 step at |O_ref| instead; every other
+    entry is held to O_TOL."""
     assert torch.isfinite(o_gpu).all(), f"non-finite O {what}"
-    eo = max_abs(o_gpu, o_ref)
+    a, r = f64(o_gpu), f64(o_ref)
+    err = (a - r).abs()
+    floor = (r.to(torch.bfloat16).to(torch.float64) - r).abs()
+    spec = floor >= O_TOL
+    eo = err[~spec].max().item() if (~spec).any() else 0.0
     el = max_abs(lse_gpu, lse_ref)
     assert eo <= O_TOL, f"O max-abs {eo:.3e} > {O_TOL} {what}"
+    if spec.any():
+        ulp = bf16_ulp(r[spec])
+        worst = (err[spec] / ulp).max().item()
+        announce(f"[spec floor] {what}: {int(spec.sum())} O entries with their own bf16 floor "
+                 f">= {O_TOL} (max floor {floor.max().item():.4e}); max error {err[spec].max().item():.4e} "
+                 f"= {worst:.3f} bf16 steps")
+        assert worst <= 1.0, f"O error {worst:.3f} bf16 steps at floor-limited entries {what}"
     assert el <= LSE_TOL, f"LSE max-abs {el:.3e} > {LSE_TOL} {what}"
     return eo, el
 
