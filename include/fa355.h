@@ -15,7 +15,8 @@
  *
  * Conventions shared by every entry point
  *   - All tensor pointers are DEVICE pointers, allocated and owned by the caller.
- *     The library allocates nothing, keeps no mutable global state and never
+ *     The library allocates nothing, keeps no mutable global state (apart from
+ *     fa_bwd_noalloc's static device array, described there) and never
  *     synchronises the device; all work is enqueued on `stream` (a hipStream_t,
  *     NULL for the default stream) in stream order and returns immediately.
  *   - q, k, v, o, dout, dq, dk, dv are bf16 (IEEE bfloat16), contiguous, with the
@@ -36,7 +37,8 @@
  *     On a validation error nothing is enqueued or written and a negative
  *     fa_status is returned.  A failed launch returns FA_ERR_LAUNCH.  Faults
  *     inside a kernel surface at the caller's next synchronisation.
- *   - Calls are reentrant and thread-safe (no shared mutable state).
+ *   - Calls are reentrant and thread-safe (no shared mutable state; fa_bwd_noalloc
+ *     calls that overlap on one GPU share its device array, see there).
  */
 #ifndef FA355_H
 #define FA355_H
@@ -122,6 +124,25 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
            const float* lse, void* dq, void* dk, void* dv, void* workspace,
            size_t workspace_bytes, int B, int H, int Nq, int Nk, int d, float scale,
            int causal, void* stream);
+
+/*
+ * Backward, dense batch, that allocates nothing: for callers that cannot call
+ * hipMalloc or pass a workspace (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation).  Arguments, results and errors as
+ * fa_bwd without the workspace.  The backward's two fp32 planes (8*B*H*Nq bytes)
+ * live instead in a static device array of FA_BWD_NOALLOC_MAX_BYTES bytes that
+ * each GPU the library runs on holds until the process ends; larger calls fail
+ * with FA_ERR_WORKSPACE.  The array's device address is looked up once per
+ * device, on the first call with that device current (FA_ERR_LAUNCH if that
+ * fails).  Every call on one GPU uses the same array: calls that may overlap on
+ * one GPU (different streams without ordering between them) race on it and
+ * give undefined gradients; stream-ordered calls are safe.  Nothing in the array
+ * needs clearing: each call writes every value it later reads.
+ */
+#define FA_BWD_NOALLOC_MAX_BYTES ((size_t)16 << 20)
+int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                   const float* lse, void* dq, void* dk, void* dv, int B, int H, int Nq, int Nk,
+                   int d, float scale, int causal, void* stream);
 
 /*
  * The backward's stages, exposed separately (dense batch only) for callers that

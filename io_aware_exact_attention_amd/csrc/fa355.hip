@@ -12,6 +12,7 @@
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "../../include/fa355.h"
@@ -196,6 +197,63 @@ AttnParams base_params(const void* q, const void* k, const void* v, int batch, i
     return p;
 }
 
+// Argument checks shared by the dense backward entry points (all but the workspace).
+int check_bwd_dense(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                    const float* lse, const void* dq, const void* dk, const void* dv, int B, int H,
+                    int Nq, int Nk, int d, float scale, int causal) {
+    if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return FA_ERR_NULL;
+    if (B <= 0 || Nq <= 0 || Nk <= 0) return FA_ERR_SHAPE;
+    int st = check_common(H, d, scale, causal);
+    if (st) return st;
+    if (causal && Nq != Nk) return FA_ERR_UNSUPPORTED;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(dout, 16) ||
+        !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(lse, 4))
+        return FA_ERR_ALIGN;
+    return check_sizes((int64_t)B * Nq, (int64_t)B * Nk, Nq, Nk, H, d, (int64_t)((Nq + 15) / 16) * H * B);
+}
+
+int launch_bwd_dense(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                     const float* lse, void* dq, void* dk, void* dv, void* workspace, int B, int H,
+                     int Nq, int Nk, float scale, int d, int causal, void* stream) {
+    AttnParams p = base_params(q, k, v, B, H, Nq, Nk, scale);
+    p.o_in = static_cast<const bf16*>(o);
+    p.dout = static_cast<const bf16*>(dout);
+    p.lse_in = lse;
+    p.dq = static_cast<bf16*>(dq);
+    p.dk = static_cast<bf16*>(dk);
+    p.dv = static_cast<bf16*>(dv);
+    set_workspace(p, workspace);
+    return launch_bwd<false>(p, d, causal, static_cast<hipStream_t>(stream));
+}
+
+// ---- no-allocation backward: the workspace lives in a static device array.
+// Each device that runs the library holds its own copy of `scratch` until the
+// process ends.  On the host the array's name only stands for the symbol; its
+// device address comes from hipGetSymbolAddress, taken once per device (with that
+// device current) and kept below.  Every call on one device uses the same
+// memory, so calls that overlap on a device (different streams, no ordering)
+// race on it.  The dQ kernel writes every row of both planes before the dK/dV
+// kernel reads them, so the array needs no clearing between calls.
+constexpr size_t kNoAllocScratchBytes = FA_BWD_NOALLOC_MAX_BYTES;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int noalloc_scratch(void** out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return FA_ERR_LAUNCH;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return FA_ERR_LAUNCH;
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return FA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -304,27 +362,25 @@ size_t fa_bwd_workspace_bytes(int batch_or_nseq, int H, int nq, int d) {
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
            const float* lse, void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
            int B, int H, int Nq, int Nk, int d, float scale, int causal, void* stream) {
-    if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return FA_ERR_NULL;
-    if (B <= 0 || Nq <= 0 || Nk <= 0) return FA_ERR_SHAPE;
-    int st = check_common(H, d, scale, causal);
+    int st = check_bwd_dense(q, k, v, o, dout, lse, dq, dk, dv, B, H, Nq, Nk, d, scale, causal);
     if (st) return st;
-    if (causal && Nq != Nk) return FA_ERR_UNSUPPORTED;
     if (!workspace || workspace_bytes < fa_bwd_workspace_bytes(B, H, Nq, d)) return FA_ERR_WORKSPACE;
-    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(dout, 16) ||
-        !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(lse, 4) ||
-        !aligned(workspace, 4))
-        return FA_ERR_ALIGN;
-    st = check_sizes((int64_t)B * Nq, (int64_t)B * Nk, Nq, Nk, H, d, (int64_t)((Nq + 15) / 16) * H * B);
+    if (!aligned(workspace, 4)) return FA_ERR_ALIGN;
+    return launch_bwd_dense(q, k, v, o, dout, lse, dq, dk, dv, workspace, B, H, Nq, Nk, scale, d,
+                            causal, stream);
+}
+
+int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                   const float* lse, void* dq, void* dk, void* dv, int B, int H, int Nq, int Nk,
+                   int d, float scale, int causal, void* stream) {
+    int st = check_bwd_dense(q, k, v, o, dout, lse, dq, dk, dv, B, H, Nq, Nk, d, scale, causal);
     if (st) return st;
-    AttnParams p = base_params(q, k, v, B, H, Nq, Nk, scale);
-    p.o_in = static_cast<const bf16*>(o);
-    p.dout = static_cast<const bf16*>(dout);
-    p.lse_in = lse;
-    p.dq = static_cast<bf16*>(dq);
-    p.dk = static_cast<bf16*>(dk);
-    p.dv = static_cast<bf16*>(dv);
-    set_workspace(p, workspace);
-    return launch_bwd<false>(p, d, causal, static_cast<hipStream_t>(stream));
+    if (fa_bwd_workspace_bytes(B, H, Nq, d) > kNoAllocScratchBytes) return FA_ERR_WORKSPACE;
+    void* ws = nullptr;
+    st = noalloc_scratch(&ws);
+    if (st) return st;
+    return launch_bwd_dense(q, k, v, o, dout, lse, dq, dk, dv, ws, B, H, Nq, Nk, scale, d, causal,
+                            stream);
 }
 
 int fa_bwd_dq_dot(const void* q, const void* k, const void* v, const void* o, const void* dout,

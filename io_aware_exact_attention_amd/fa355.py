@@ -2,7 +2,7 @@
 
 The functions named like the C entry points (``fa_fwd``, ``fa_fwd_persistent``,
 ``fa_bwd`` and its stages ``fa_bwd_dq_dot`` / ``fa_bwd_dot`` / ``fa_bwd_dkdv`` /
-``fa_bwd_dq``,
+``fa_bwd_dq``, ``fa_bwd_noalloc`` (the backward without a caller workspace),
 ``fa_fwd_varlen``, ``fa_bwd_varlen``, ``fa_fwd_decode``, ``fa_fwd_fp8``,
 ``fa_fwd_fp8_codes``, the ``*_workspace_bytes`` queries, ``fa_status_string``)
 take torch tensors that already live on the GPU, pass their device pointers and
@@ -36,6 +36,7 @@ _SIGNATURES = {
     "fa_fwd_varlen": (_c_int, [_vp] * 7 + [_c_int] * 5 + [_c_float, _c_int, _vp]),
     "fa_bwd_workspace_bytes": (_sz, [_c_int] * 4),
     "fa_bwd": (_c_int, [_vp] * 10 + [_sz] + [_c_int] * 5 + [_c_float, _c_int, _vp]),
+    "fa_bwd_noalloc": (_c_int, [_vp] * 9 + [_c_int] * 5 + [_c_float, _c_int, _vp]),
     "fa_bwd_varlen": (_c_int, [_vp] * 10 + [_sz] + [_vp] * 2 + [_c_int] * 5 + [_c_float, _c_int, _vp]),
     "fa_bwd_dot": (_c_int, [_vp] * 4 + [_sz] + [_c_int] * 4 + [_vp]),
     "fa_bwd_dkdv": (_c_int, [_vp] * 5 + [_sz] + [_vp] * 2 + [_c_int] * 5 + [_c_float, _c_int, _vp]),
@@ -50,6 +51,9 @@ _SIGNATURES = {
 
 STATUS = {0: "FA_OK", -1: "FA_ERR_NULL", -2: "FA_ERR_SHAPE", -3: "FA_ERR_UNSUPPORTED",
           -4: "FA_ERR_ALIGN", -5: "FA_ERR_LAUNCH", -6: "FA_ERR_WORKSPACE"}
+
+# bytes of fa_bwd_noalloc's static device array (FA_BWD_NOALLOC_MAX_BYTES in fa355.h)
+FA_BWD_NOALLOC_MAX_BYTES = 16 << 20
 
 _lib = None
 
@@ -188,6 +192,14 @@ def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, scale: float, causal: b
     _check(lib().fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq),
                         _ptr(dk), _ptr(dv), _ptr(workspace), nbytes, B, H, Nq, Nk, d,
                         float(scale), int(bool(causal)), _stream(stream)))
+
+
+def fa_bwd_noalloc(q, k, v, o, dout, lse, dq, dk, dv, scale: float, causal: bool, stream=None):
+    B, H, Nq, Nk, d = _check_dense(q, k, v, o, lse,
+                                   (("dout", dout, "q"), ("dq", dq, "q"), ("dk", dk, "k"), ("dv", dv, "k")))
+    _check(lib().fa_bwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq),
+                                _ptr(dk), _ptr(dv), B, H, Nq, Nk, d, float(scale), int(bool(causal)),
+                                _stream(stream)))
 
 
 def fa_bwd_dq_dot(q, k, v, o, dout, lse, workspace, dq, scale: float, causal: bool, stream=None):

@@ -186,3 +186,16 @@ def test_binding_raises_on_error():
     with pytest.raises(fa355.FaError) as e:
         fa355._check(-3)
     assert e.value.status == -3
+
+
+def test_noalloc_limit_matches_header_and_rejects_larger_calls():
+    import re
+    text = open(fa355.HEADER).read()
+    m = re.search(r"#define FA_BWD_NOALLOC_MAX_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == fa355.FA_BWD_NOALLOC_MAX_BYTES
+    n_rows = fa355.FA_BWD_NOALLOC_MAX_BYTES // 8 + 1   # 8 workspace bytes per (batch, head, row)
+    f = fa355.lib().fa_bwd_noalloc
+    assert f(*[A] * 9, 1, 1, n_rows, n_rows, 64, 0.125, 0, None) == -6   # FA_ERR_WORKSPACE
+    assert f(*[A] * 8, None, 1, 1, 16, 16, 64, 0.125, 0, None) == -1     # FA_ERR_NULL
+    assert f(*[A] * 9, 1, 1, 16, 8, 64, 0.125, 1, None) == -3            # causal, Nq != Nk
+    assert f(*[A] * 8, MIS, 1, 1, 16, 16, 64, 0.125, 0, None) == -4      # misaligned dv
