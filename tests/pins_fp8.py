@@ -334,6 +334,119 @@ def pin_fp8_forward_close_and_rotation_helps(f):
     assert e_rot < e_plain, (e_rot, e_plain)
 
 
+def _fwht32(x):
+    """Fast Walsh-Hadamard transform along the last axis in float32 (butterflies
+    of stride 1, 2, 4, ...: each stage rounds once), the transform the page's
+    rotation needs, computed the way a GPU computes it."""
+    d = x.shape[-1]
+    y = x.to(torch.float32)
+    h = 1
+    while h < d:
+        y = y.reshape(*x.shape[:-1], d // (2 * h), 2, h)
+        a, b = y[..., 0, :], y[..., 1, :]
+        y = torch.stack([a + b, a - b], dim=-2).reshape(*x.shape[:-1], d)
+        h *= 2
+    return y.to(torch.float64)
+
+
+def pin_fp8_rotation_error_bound(f):
+    # the bound on |fp32 rotation - exact| / s holds for every element of random
+    # rows and of rows whose partial sums keep growing (x_i = sigma_i (1 + u_i 2^-6),
+    # so every butterfly adds like-signed terms), and on the latter it is within a
+    # factor 5 of the worst element of some row (not a loose bound that any
+    # rotation error passes); a different power-of-two scale in each 64-row block
+    d = 128
+    g = torch.Generator().manual_seed(414)
+    sg = (torch.randint(0, 2, (d,), generator=g) * 2 - 1).to(torch.float64)
+    rnd = torch.randn(1, 256, 1, d, generator=g, dtype=torch.float32).to(torch.float64)
+    u = torch.rand(1, 256, 1, d, generator=g, dtype=torch.float32).to(torch.float64)
+    coh = (sg * (1 + u * 2.0 ** -6)).to(torch.float32).to(torch.float64)
+    s = torch.tensor([[[0.125, 0.25, 0.0625, 0.5]]], dtype=torch.float64)
+    rows = s.repeat_interleave(64, dim=2).transpose(1, 2)[..., None]          # [1, 256, 1, 1]
+    for x, tight in ((rnd, False), (coh, True)):
+        err = (_fwht32(x * sg) - f.rotate(x, sg)).abs() / rows
+        bnd = f.fp32_rotation_error(x, sg, s)
+        assert bnd.shape == (1, 256, 1, 1)
+        assert bool((err <= bnd).all())
+        if tight:
+            assert (bnd / err.amax(-1, keepdim=True)).min().item() <= 5.0
+
+
+def _vec(vals):
+    """[1, n, 1, 4] with the first component of each row set (exact e4m3 values
+    or pre-rounding values)."""
+    t = torch.zeros(1, len(vals), 1, 4, dtype=torch.float64)
+    t[0, :, 0, 0] = torch.tensor([float(v) for v in vals], dtype=torch.float64)
+    return t
+
+
+def _flip_bounds(d_o, d_l, so, sl, what, ds=0.0):
+    """One near-tie code rounded the other way moves O by d_o and LSE by d_l: the
+    slack covers that move and is at most 1.5 times it (not inflated).  The
+    slack is a first-order bound: a flip that moves a score by ds leaves a
+    second-order remainder of relative size at most about ds, allowed here."""
+    so, sl = float(so), float(sl)
+    allow = 1.0 + ds + 1e-6
+    assert d_o <= allow * so + 1e-12, (what, d_o, so)
+    assert so <= 1.5 * d_o + 1e-12, (what, d_o, so)
+    if d_l > 1e-9:
+        assert d_l <= allow * sl + 1e-12 and sl <= 1.5 * d_l, (what, d_l, sl)
+    else:
+        assert sl == 0.0, (what, sl)
+
+
+def pin_fp8_tie_slack_single_flip(f):
+    # one query, two keys, values only in component 0; exactly one code of each
+    # kind sits at a near-tie (within 1e-7 relative of a midpoint).  For P and V
+    # the oracle's own output with the code rounded each way is compared (P,
+    # through a score scale just below / above the tie); for Q and K, whose flip
+    # also re-rounds the probabilities, the exact dense attention on the decoded
+    # inputs with either code (the slack bounds the score effect, to first order)
+    enc, dec = f.e4m3_encode, f.e4m3_decode
+    one = torch.ones(1, 1, dtype=torch.float64)
+    # P: keys 2, 1 (q = 1), scores 2c, c; 16 exp(-c) = 12.5 is the midpoint of the
+    # codes 12 and 13, so P~_1 rounds to 12 or 13 as c crosses c0; values 1, 3
+    q8, k8, v8 = enc(_vec([1.0])), enc(_vec([2.0, 1.0])), enc(_vec([1.0, 3.0]))
+    c0 = math.log(16.0 / 12.5)
+    res = [f.fp8_attention_forward(q8, k8, v8, one, one, one, c, False, block=None)
+           for c in (c0 * (1 + 1e-9), c0 * (1 - 1e-9))]
+    assert f.RESCALE_LOG2 == 4.0
+    _flip_bounds((res[1][0] - res[0][0]).abs()[0, 0, 0, 0].item(),
+                 (res[1][1] - res[0][1]).abs().item(), res[0][2][0, 0, 0, 0], res[0][3][0, 0, 0], "P")
+    assert res[0][2][0, 0, 0, 1:].abs().max().item() == 0.0
+    # V: scores 0, -ln 2 give exact P~ 1, 1/2; v_1 = 2.625 (1 + 1e-7) lies at the
+    # midpoint of 2.5 and 2.75 (in units of V's scale, 0.5)
+    vs = _vec([-2.0, 2.625 * (1 + 1e-7)])
+    q8, k8 = enc(_vec([1.0])), enc(_vec([0.0, -1.0]))
+    v8, v8alt = enc(vs), enc(_vec([-2.0, 2.5]))
+    assert dec(v8)[0, 1, 0, 0].item() == 2.75
+    sv = one * 0.5                                    # V in units of its scale
+    o, lse, so, sl = f.fp8_attention_forward(q8, k8, v8, one, one, sv, math.log(2.0), False,
+                                             v_scaled=vs, block=None)
+    oa, lsea, _, _ = f.fp8_attention_forward(q8, k8, v8alt, one, one, sv, math.log(2.0), False, block=None)
+    _flip_bounds((oa - o).abs()[0, 0, 0, 0].item(), (lsea - lse).abs().item(), so[0, 0, 0, 0], sl[0, 0, 0], "V")
+    # Q: q_0 = 1.0625 (1 + 1e-7), the midpoint of 1 and 1.125; keys 0, -1 (so only
+    # the second score moves), values -2, 3 (on either side of O = -1, so the first-
+    # order bound is tight)
+    qs, ks, vs = _vec([1.0625 * (1 + 1e-7)]), _vec([0.0, -1.0]), _vec([-2.0, 3.0])
+    q8, q8alt, k8, v8 = enc(qs), enc(_vec([1.0])), enc(ks), enc(vs)
+    o, lse, so, sl = f.fp8_attention_forward(q8, k8, v8, one, one, one, 1.25, False, q_scaled=qs,
+                                             k_scaled=ks, block=None, p_tie_rel=0.0)
+    e0 = dense.attention_forward(dec(q8), dec(k8), dec(v8), 1.25, False)
+    e1 = dense.attention_forward(dec(q8alt), dec(k8), dec(v8), 1.25, False)
+    _flip_bounds((e1[0] - e0[0]).abs()[0, 0, 0, 0].item(), (e1[1] - e0[1]).abs().item(),
+                 so[0, 0, 0, 0], sl[0, 0, 0], "Q", ds=1.25 * 0.125)
+    # K: q = -1, k_1 = 1.0625 (1 + 1e-7), the same midpoint
+    qs, ks = _vec([-1.0]), _vec([0.0, 1.0625 * (1 + 1e-7)])
+    q8, k8, k8alt = enc(qs), enc(ks), enc(_vec([0.0, 1.0]))
+    o, lse, so, sl = f.fp8_attention_forward(q8, k8, v8, one, one, one, 1.25, False, q_scaled=qs,
+                                             k_scaled=ks, block=None, p_tie_rel=0.0)
+    e0 = dense.attention_forward(dec(q8), dec(k8), dec(v8), 1.25, False)
+    e1 = dense.attention_forward(dec(q8), dec(k8alt), dec(v8), 1.25, False)
+    _flip_bounds((e1[0] - e0[0]).abs()[0, 0, 0, 0].item(), (e1[1] - e0[1]).abs().item(),
+                 so[0, 0, 0, 0], sl[0, 0, 0], "K", ds=1.25 * 0.125)
+
+
 ALL_PINS = [
     pin_e4m3_named_codes,
     pin_e4m3_encode_is_nearest,
@@ -347,4 +460,6 @@ ALL_PINS = [
     pin_fp8_attention_p_rounding_bound,
     pin_fp8_slack_covers_p_rounding,
     pin_fp8_forward_close_and_rotation_helps,
+    pin_fp8_rotation_error_bound,
+    pin_fp8_tie_slack_single_flip,
 ]

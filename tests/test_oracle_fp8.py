@@ -73,6 +73,27 @@ MUTATIONS = {
     "rotation_norm_missing": ("qk_scale = scale / d if rotate_qk else scale",
                               "qk_scale = scale"),
     "v_rotated_too": ("v8, sv, vs = quantize_e4m3(v, None)", "v8, sv, vs = quantize_e4m3(v, sg)"),
+    # the slack's own terms and the rotation's rounding bound
+    "rotation_error_no_log2d": ("return math.log2(d) * 2.0 ** -24 * l1", "return 2.0 ** -24 * l1"),
+    "rotation_error_x4": ("return math.log2(d) * 2.0 ** -24 * l1", "return 4 * math.log2(d) * 2.0 ** -24 * l1"),
+    "rotation_error_x2": ("return math.log2(d) * 2.0 ** -24 * l1", "return 2 * math.log2(d) * 2.0 ** -24 * l1"),
+    "rotation_error_ignores_scale": ("l1 / row_scales(s, N, block_rows).transpose(1, 2)[..., None]", "l1"),
+    "rotation_error_fp64_eps": ("return math.log2(d) * 2.0 ** -24 * l1", "return math.log2(d) * 2.0 ** -53 * l1"),
+    "slack_drops_ds": ("so + dev)", "so)"),
+    "slack_o_x4": ("so + dev)", "4 * (so + dev))"),
+    "slack_l_x4": ("slack_l[b, h] = (p_true * ds).sum(dim=-1)", "slack_l[b, h] = 4 * (p_true * ds).sum(dim=-1)"),
+    "slack_l_dropped": ("slack_l[b, h] = (p_true * ds).sum(dim=-1)", "slack_l[b, h] = 0.0 * (p_true * ds).sum(dim=-1)"),
+    "slack_drops_tie_v": ("so = (tie_p + tie_v) / p_scale * linv", "so = tie_p / p_scale * linv"),
+    "slack_drops_tie_p": ("so = (tie_p + tie_v) / p_scale * linv", "so = tie_v / p_scale * linv"),
+    "k_ties_ignored": ("tq, tk = tie_steps(q_scaled, q8, q_tie_atol), tie_steps(k_scaled, k8, k_tie_atol)",
+                       "tq, tk = tie_steps(q_scaled, q8, q_tie_atol), tie_steps(None, k8)"),
+    "q_ties_ignored": ("tq, tk = tie_steps(q_scaled, q8, q_tie_atol), tie_steps(k_scaled, k8, k_tie_atol)",
+                       "tq, tk = tie_steps(None, q8), tie_steps(k_scaled, k8, k_tie_atol)"),
+    "ds_k_signed": ("torch.matmul(tq[b, :, h], kh.abs().transpose(0, 1))", "torch.matmul(tq[b, :, h], kh.transpose(0, 1))"),
+    "ds_q_signed": ("torch.matmul(qh.abs(), tk[b, :, h].transpose(0, 1))", "torch.matmul(qh, tk[b, :, h].transpose(0, 1))"),
+    "dev_drops_o_term": ("dev = torch.matmul(p_true * ds, vabs) + (p_true * ds).sum(-1, keepdim=True) * o[b, :, h].abs()",
+                         "dev = torch.matmul(p_true * ds, vabs)"),
+    "tie_v_unscaled": ("tvh = tv[b, :, h] * rv[b, h][:, None]", "tvh = tv[b, :, h]"),
 }
 
 

@@ -13,6 +13,13 @@ sits at a near-tie of its threshold have infinite O slack: either decision is a
 correct execution.  They must stay rare (at most 1% of rows; none occur in these
 cases) and keep the LSE bar.
 
+End to end, at full size and on N(0,1) inputs the output is also held to an
+a-priori error model against exact attention (tests/fp8_apriori.py): every
+e4m3 rounding an independent uniform error within its half-step, propagated to
+first order; |O - O_exact| <= 6 sigma + bf16 rounding.  That bound shares
+nothing with the FP8 oracle, so a mistake common to the oracle and the kernel
+cannot pass it.
+
 The quantisation itself is checked code by code: the per-block scales are equal and every
 code equals the oracle's, except where the oracle's value lies within the fp32
 rotation bound of a midpoint, where the neighbouring code is accepted.  The
@@ -28,6 +35,7 @@ import torch
 import oracle.fp8 as of8
 from oracle import attention_forward as exact_forward
 from io_aware_exact_attention_amd import fa355, workloads as wl
+from tests import fp8_apriori as ap
 from tests import gpu_util as gu
 
 pytestmark = pytest.mark.gpu
@@ -176,6 +184,11 @@ def test_fp8_end_to_end(case, rotate):
     o_ref, lse_ref, so, sl, _, _ = of8.fp8_forward(x["q"], x["k"], x["v"], x["signs"], scale, causal,
                                                    rotate, TIE_REL, fp32_rotation=True)
     _check(o, lse, o_ref, lse_ref, so, sl, f"end to end {case} rotate={rotate}")
+    # and against exact attention, within the a-priori e4m3 error model (which
+    # shares nothing with the FP8 oracle's algorithm or design choices)
+    ref = ap.fp8_sigma(x["q"], x["k"], x["v"], x["signs"], scale, causal, rotate)
+    r_o, r_l, rms, outside = ap.check_apriori(o, lse, *ref, what=f"end to end {case} rotate={rotate}")
+    assert outside == 0.0
 
 
 def test_fp8_deterministic():
@@ -204,12 +217,15 @@ def test_fp8_error_against_exact_and_rotation_helps():
     e_rot, e_pl = of8.rmse(o_rot, o_ex), of8.rmse(o_pl, o_ex)
     print(f"[fp8] rmse vs exact: rotated {e_rot:.3e}, unrotated {e_pl:.3e}", flush=True)
     assert e_rot < e_pl
-    # and without outliers the FP8 forward stays within a few e4m3 steps of exact
+    # and without outliers every element of the FP8 forward lies within the
+    # a-priori e4m3 error model's bound of exact attention
     y = _inputs(B, N, N, H, seed=3301)
-    o_ex2, _ = exact_forward(y["q"], y["k"], y["v"], 128 ** -0.5, True)
-    e2 = of8.rmse(_run_full(y, 128 ** -0.5, True, True)[0], o_ex2)
-    print(f"[fp8] rmse vs exact, N(0,1) inputs: {e2:.3e}", flush=True)
-    assert e2 < 3e-2
+    o2, lse2, _ = _run_full(y, 128 ** -0.5, True, True)
+    ref = ap.fp8_sigma(y["q"], y["k"], y["v"], y["signs"], 128 ** -0.5, True, True)
+    r_o, r_l, rms, outside = ap.check_apriori(o2, lse2, *ref, what="N(0,1) inputs")
+    print(f"[fp8] N(0,1) inputs: rmse vs exact {of8.rmse(o2, ref[0]):.3e}; largest error "
+          f"{r_o:.2f} (O) / {r_l:.2f} (LSE) of the a-priori bound, rms error/sigma {rms:.2f}", flush=True)
+    assert outside == 0.0
 
 
 def test_fp8_workload_full_size_sampled():
@@ -227,6 +243,9 @@ def test_fp8_workload_full_size_sampled():
             x["q"][b:b + 1, :, sl_], x["k"][b:b + 1, :, sl_], x["v"][b:b + 1, :, sl_], x["signs"],
             base.scale, True, True, TIE_REL, fp32_rotation=True)
         _check(o[b:b + 1, :, sl_], lse[b:b + 1, sl_], o_ref, lse_ref, so, sl, f"full size b{b} h{h}")
+        ref = ap.fp8_sigma(x["q"][b:b + 1, :, sl_], x["k"][b:b + 1, :, sl_], x["v"][b:b + 1, :, sl_],
+                           x["signs"], base.scale, True, True)
+        ap.check_apriori(o[b:b + 1, :, sl_], lse[b:b + 1, sl_], *ref, what=f"full size b{b} h{h}")
 
 
 @pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
