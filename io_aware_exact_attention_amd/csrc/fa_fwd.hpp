@@ -51,6 +51,13 @@ struct FwdCfg {
 
 // One work item: query tile `tile` of (batch or sequence, head) pair `bh`, with
 // the work-group's LDS at `smem`.
+//
+// Software-pipelined over key tiles: the scores of tile t+1 are formed while tile
+// t's probabilities are exponentiated, and tile t's P V product runs while tile
+// t+1's row maximum is reduced, so each wave keeps the matrix unit and the
+// vector unit busy at once instead of alternating between them.  K tiles and V
+// tiles therefore live one tile apart in two double buffers: when iteration t
+// starts, K(t+1) and V(t) are in LDS and the loads of K(t+2) and V(t+1) go out.
 template <int D, bool CAUSAL, bool VARLEN>
 __device__ __forceinline__ void fwd_tile(const AttnParams& p, char* smem, int bh, int tile) {
     using C = FwdCfg<D>;
@@ -58,6 +65,8 @@ __device__ __forceinline__ void fwd_tile(const AttnParams& p, char* smem, int bh
     const int wave = threadIdx.x >> 6;
     const int h2 = lane >> 5;
     const int col = lane & 31;
+    const int sl = lane & 15;
+    const int g = (lane >> 4) & 1;
 
     const int h = bh % p.H;
     const int b = bh / p.H;
@@ -66,7 +75,7 @@ __device__ __forceinline__ void fwd_tile(const AttnParams& p, char* smem, int bh
     const int q_start = tile * C::BM;
     if (q_start >= nq) return;
     const int kv_end = CAUSAL ? min(nk, q_start + C::BM) : nk;
-    const int n_kv = (kv_end + C::BN - 1) / C::BN;
+    const int n_kv = (kv_end + C::BN - 1) / C::BN;   // the work-group's key tiles
     const int64_t tok = (int64_t)p.H * D;
     const bf16* kbase = p.k + (int64_t)ks * tok + h * D;
     const bf16* vbase = p.v + (int64_t)ks * tok + h * D;
@@ -78,6 +87,10 @@ __device__ __forceinline__ void fwd_tile(const AttnParams& p, char* smem, int bh
 
     const int qw0 = q_start + wave * 32;   // first query row of this wave
     const int qi = qw0 + col;              // this lane's query row
+    // this wave's key tiles: under the causal mask the ones that start at or
+    // before its last row.  Only the last of them can need a mask (the diagonal
+    // tile, or the ragged tail of the keys).
+    const int n_w = CAUSAL ? min(n_kv, (qw0 + 31) / C::BN + 1) : n_kv;
     const bf16* qptr = p.q + (int64_t)(qs + min(qi, nq - 1)) * tok + h * D + 8 * h2;
     bf16x8 qf[C::KSTEPS];
 #pragma unroll
@@ -91,129 +104,97 @@ __device__ __forceinline__ void fwd_tile(const AttnParams& p, char* smem, int bh
     float m = kNegInf;   // running max of raw scores q.k (this row)
     float l = 0.f;       // running sum, over the keys this lane holds (gives LSE)
     float lr = 0.f;      // the same sum of the bf16-rounded P~ that the P V product uses
+    float alpha = 0.f;   // e^(m_old - m) of the tile whose scores are held
+    float mc = 0.f;      // reference maximum * scale * log2(e) of that tile
     const float c = p.scale_log2;
 
+    // LDS: buffer j (j = 0, 1) holds a K tile at 2 j TILE_BYTES and a V tile
+    // TILE_BYTES after it.  K(t) sits in buffer t % 2, V(t) in buffer t % 2.
     if (n_kv > 0) {
         loader.load(ldsb, kbase, kv_bytes, 0, wave_s);
         loader.load(ldsb + C::TILE_BYTES, vbase, kv_bytes, 0, wave_s);
     }
+    if (n_kv > 1) loader.load(ldsb + 2 * C::TILE_BYTES, kbase, kv_bytes, C::BN * row_bytes, wave_s);
+
     // per-lane byte offsets of the K operand reads (one per k-step) within a tile
     int koff[C::KSTEPS];
 #pragma unroll
     for (int st = 0; st < C::KSTEPS; ++st) koff[st] = tile_off<D>(col, 2 * st + h2);
-    // One key tile.  The loop below runs two per trip, so that each tile's LDS
-    // buffer is a compile-time constant: it goes into the LDS reads' immediate
-    // offsets instead of costing vector adds per operand read (2-3% measured).
-    auto step = [&](int t, auto buf) __attribute__((always_inline)) {
-        constexpr int KB0 = decltype(buf)::value * 2 * C::TILE_BYTES;   // this tile's buffer
-        constexpr int KB1 = (1 - decltype(buf)::value) * 2 * C::TILE_BYTES;
-        const FA_LDS char* kt = ldsb + KB0;
-        const FA_LDS char* vt = kt + C::TILE_BYTES;
-        wait_vmem();
-        __syncthreads();
-        if (t + 1 < n_kv) {
-            loader.load(ldsb + KB1, kbase, kv_bytes, (t + 1) * C::BN * row_bytes, wave_s);
-            loader.load(ldsb + KB1 + C::TILE_BYTES, vbase, kv_bytes, (t + 1) * C::BN * row_bytes, wave_s);
-        }
-        const int kv0 = t * C::BN;
-        if (CAUSAL && kv0 > qw0 + 31) return;   // every key here is above this wave's rows
 
-        // S^T[key][query] = K Q^T for the tile's 64 keys
-        f32x16 s[C::KB];
+    // S^T[key][query] = K Q^T for the 64 keys of the K tile at `kt`
+    auto scores = [&](const FA_LDS char* kt, f32x16 (&sc)[C::KB]) __attribute__((always_inline)) {
 #pragma unroll
         for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
-        bf16x8 ka[C::KSTEPS][C::KB];
+            for (int r = 0; r < 16; ++r) sc[kb][r] = 0.f;
 #pragma unroll
         for (int st = 0; st < C::KSTEPS; ++st)
 #pragma unroll
-            for (int kb = 0; kb < C::KB; ++kb)
-                // row kb*32 + col: 32 more rows keep the swizzle
-                ka[st][kb] = lds_read16(kt + koff[st] + kb * 32 * C::ROW_BYTES);
+            for (int kb = 0; kb < C::KB; ++kb)   // row kb*32 + col: 32 more rows keep the swizzle
+                sc[kb] = mfma_32x32x16(lds_read16(kt + koff[st] + kb * 32 * C::ROW_BYTES), qf[st], sc[kb]);
+    };
+    // causal diagonal / ragged tail of key tile t
+    auto mask = [&](f32x16 (&sc)[C::KB], int t) __attribute__((always_inline)) {
+        const int kv0 = t * C::BN;
 #pragma unroll
-        for (int st = 0; st < C::KSTEPS; ++st)
+        for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
-            for (int kb = 0; kb < C::KB; ++kb)
-                s[kb] = mfma_32x32x16(ka[st][kb], qf[st], s[kb]);
-        {   // keep AHEAD operand reads in flight ahead of the products (as compiled,
-            // each product otherwise waited for its own read: 1.3% on the forward)
-            constexpr int NR = C::KSTEPS * C::KB, AHEAD = 6;
-            __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);
-#pragma unroll
-            for (int i = 0; i < NR - AHEAD; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            for (int r = 0; r < 16; ++r) {
+                const int key = kv0 + kb * 32 + 8 * (r >> 2) + 4 * h2 + (r & 3);
+                if ((CAUSAL && key > qi) || key >= nk) sc[kb][r] = kNegInf;
             }
-            __builtin_amdgcn_sched_group_barrier(0x008, AHEAD, 0);
-        }
-
-        // causal diagonal / ragged tail
-        const bool need_mask = (CAUSAL && kv0 + C::BN - 1 > qw0) || (kv0 + C::BN > nk);
-        if (need_mask) {
-#pragma unroll
-            for (int kb = 0; kb < C::KB; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = kv0 + kb * 32 + 8 * (r >> 2) + 4 * h2 + (r & 3);
-                    if ((CAUSAL && key > qi) || key >= nk) s[kb][r] = kNegInf;
-                }
-        }
-
+    };
+    // new running maximum from the held scores: sets m, alpha, mc
+    auto row_max = [&](const f32x16 (&sc)[C::KB]) __attribute__((always_inline)) {
         float mx = kNegInf;
 #pragma unroll
         for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb][r]);
         mx = max_halves(mx);
         const float m_new = fmaxf(m, mx);
         const float m_ref = (m_new == kNegInf) ? 0.f : m_new;
-        const float alpha = fast_exp2((m - m_ref) * c);
-        const float mc = m_ref * c;
+        alpha = fast_exp2((m - m_ref) * c);
+        mc = m_ref * c;
+        m = m_new;
+    };
+    // P~ = exp2(S c - m c) of the held scores, packed to bf16 as the P^T operand
+    // (registers 8*(ks&1)..+7 of key block ks/2 hold keys 16*ks + {4*h2 + 0..3,
+    // 8 + 4*h2 + 0..3} of this lane's query); updates l and lr.  O is
+    // normalised by the sum of the rounded values it was formed from, so that
+    // O = sum_j bf16(P~_j) v_j / sum_j bf16(P~_j) is a convex combination of the
+    // v_j, whose error from P's rounding scales with v_j - O rather than v_j.
+    auto probs = [&](f32x16 (&sc)[C::KB], bf16x8 (&pk)[C::BN / 16]) __attribute__((always_inline)) {
         float rs = 0.f;
 #pragma unroll
         for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const float pr = fast_exp2(__builtin_fmaf(s[kb][r], c, -mc));
-                s[kb][r] = pr;
+                const float pr = fast_exp2(__builtin_fmaf(sc[kb][r], c, -mc));
+                sc[kb][r] = pr;
                 rs += pr;
             }
         l = l * alpha + rs;
-        m = m_new;
-        if (wave_any(alpha != 1.f)) {
-#pragma unroll
-            for (int cb = 0; cb < C::DBLK; ++cb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) acc[cb][r] *= alpha;
-        }
-
-        // P^T operand: registers 8*(ks&1)..+7 of key block ks/2 hold keys
-        // 16*ks + {4*h2 + 0..3, 8 + 4*h2 + 0..3} for this lane's query.
-        bf16x8 pk[C::BN / 16];
+        float rr = lr * alpha;
 #pragma unroll
         for (int ks2 = 0; ks2 < C::BN / 16; ++ks2) {
             float tmp[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) tmp[e] = s[ks2 >> 1][8 * (ks2 & 1) + e];
+            for (int e = 0; e < 8; ++e) tmp[e] = sc[ks2 >> 1][8 * (ks2 & 1) + e];
             pk[ks2] = pack8(tmp);
+            rr = sum8_bf16(pk[ks2], rr);
         }
-        // O is normalised by the sum of the probabilities it was formed from:
-        // O = sum_j bf16(P~_j) v_j / sum_j bf16(P~_j) is a convex combination of
-        // the v_j, whose error from P's rounding scales with v_j - O rather than v_j
-        float rr = lr * alpha;
-#pragma unroll
-        for (int ks2 = 0; ks2 < C::BN / 16; ++ks2) rr = sum8_bf16(pk[ks2], rr);
         lr = rr;
-
-        // O^T[dim][query] += V^T P^T; V^T operand via transposed LDS reads of the
-        // same key order: rows 16*ks + 4*h2 + 0..3 and +8.
-        const int sl = lane & 15;
-        const int g = (lane >> 4) & 1;
+    };
+    // O^T[dim][query] = alpha O^T + V^T P^T; V^T operand via transposed LDS reads
+    // of the same key order: rows 16*ks + 4*h2 + 0..3 and +8
+    auto pv = [&](const FA_LDS char* vt, const bf16x8 (&pk)[C::BN / 16]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int ks2 = 0; ks2 < C::BN / 16; ++ks2) {
+        for (int cb = 0; cb < C::DBLK; ++cb) {
 #pragma unroll
-            for (int cb = 0; cb < C::DBLK; ++cb) {
+            for (int r = 0; r < 16; ++r) acc[cb][r] *= alpha;
+#pragma unroll
+            for (int ks2 = 0; ks2 < C::BN / 16; ++ks2) {
                 const int c0 = cb * 32 + 16 * g;
                 const int rk = ks2 * 16 * C::ROW_BYTES;   // 16 more rows keep the swizzle
                 bf16x8 a = join(lds_read_tr(vt + tr_off<D>(4 * h2, c0, sl) + rk),
@@ -222,9 +203,58 @@ __device__ __forceinline__ void fwd_tile(const AttnParams& p, char* smem, int bh
             }
         }
     };
+
+    f32x16 s[C::KB];   // scores of the tile the loop is at
+    wait_vmem();
+    __syncthreads();
+    if (n_w > 0) {
+        scores(ldsb, s);
+        if (n_w == 1) mask(s, 0);
+        row_max(s);
+    }
+    // Iteration t: exponentiate the held S(t), form S(t+1), then O += P(t) V(t)
+    // and the maximum of S(t+1).  Two per trip of the loop below, so that every
+    // LDS buffer offset is a compile-time constant.
+    auto iter = [&](int t, auto par) __attribute__((always_inline)) {
+        constexpr int PB = decltype(par)::value;   // t % 2
+        const FA_LDS char* k_next = ldsb + (1 - PB) * 2 * C::TILE_BYTES;   // K(t+1)
+        const FA_LDS char* v_cur = ldsb + PB * 2 * C::TILE_BYTES + C::TILE_BYTES;   // V(t)
+        wait_vmem();
+        __syncthreads();
+        if (t + 2 < n_kv)   // K(t+2) replaces K(t), whose scores every wave has formed
+            loader.load(ldsb + PB * 2 * C::TILE_BYTES, kbase, kv_bytes, (t + 2) * C::BN * row_bytes, wave_s);
+        if (t + 1 < n_kv)   // V(t+1) replaces V(t-1), whose product every wave has formed
+            loader.load(ldsb + (1 - PB) * 2 * C::TILE_BYTES + C::TILE_BYTES, vbase, kv_bytes,
+                        (t + 1) * C::BN * row_bytes, wave_s);
+        if (t >= n_w) return;
+        // one basic block per case (the compiler interleaves its products with its
+        // vector work only within a block).  O's rescale is unconditional: under
+        // the causal mask of B8 H16 N4096 some row of a 32-row wave moves its
+        // maximum in 78% of tiles, and its multiplies sit among the products.
+        auto full = [&](auto masked) __attribute__((always_inline)) {
+            bf16x8 pk[C::BN / 16];
+            f32x16 sn[C::KB];
+            probs(s, pk);
+            scores(k_next, sn);
+            pv(v_cur, pk);
+            if constexpr (decltype(masked)::value) mask(sn, t + 1);
+            row_max(sn);
+#pragma unroll
+            for (int kb = 0; kb < C::KB; ++kb) s[kb] = sn[kb];
+        };
+        if (t + 2 < n_w) {
+            full(std::false_type{});
+        } else if (t + 2 == n_w) {   // S(t+1) is the wave's last tile: masked
+            full(std::true_type{});
+        } else {                     // the wave's last tile
+            bf16x8 pk[C::BN / 16];
+            probs(s, pk);
+            pv(v_cur, pk);
+        }
+    };
     for (int t = 0; t < n_kv; t += 2) {
-        step(t, std::integral_constant<int, 0>{});
-        if (t + 1 < n_kv) step(t + 1, std::integral_constant<int, 1>{});
+        iter(t, std::integral_constant<int, 0>{});
+        if (t + 1 < n_kv) iter(t + 1, std::integral_constant<int, 1>{});
     }
 
     const float lt = sum_halves(l);
