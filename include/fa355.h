@@ -72,6 +72,10 @@ int fa_version(void);
  *   lse [B,H,Nq] fp32 (written)
  *   scale: multiplies Q K^T (1/sqrt(d) for standard attention); must be finite and > 0.
  *   causal: 0 or 1.
+ * When the query tiles (128 rows) of all (batch, head) pairs fit on the GPU at
+ * once (two work-groups per CU), this runs fa_fwd_persistent's kernel, whose
+ * longest-first deal balances a single round better than dispatch order does;
+ * otherwise one work-group per query tile.  The results are the same bit for bit.
  */
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            int B, int H, int Nq, int Nk, int d, float scale, int causal, void* stream);

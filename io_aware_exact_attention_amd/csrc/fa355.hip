@@ -254,6 +254,48 @@ int noalloc_scratch(void** out) {
     return FA_OK;
 }
 
+// Dense forward arguments -> kernel parameters (shared by fa_fwd and fa_fwd_persistent).
+int prepare_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq,
+                int Nk, int d, float scale, int causal, AttnParams* out) {
+    if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+    if (B <= 0 || Nq <= 0 || Nk <= 0) return FA_ERR_SHAPE;
+    int st = check_common(H, d, scale, causal);
+    if (st) return st;
+    if (causal && Nq != Nk) return FA_ERR_UNSUPPORTED;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
+        return FA_ERR_ALIGN;
+    const int ntq = (Nq + FwdCfg<128>::BM - 1) / FwdCfg<128>::BM;
+    st = check_sizes((int64_t)B * Nq, (int64_t)B * Nk, Nq, Nk, H, d, (int64_t)ntq * H * B);
+    if (st) return st;
+    *out = base_params(q, k, v, B, H, Nq, Nk, scale);
+    out->o = static_cast<bf16*>(o);
+    out->lse = lse;
+    out->n_tiles = ntq;
+    return FA_OK;
+}
+
+// Work-group slots of the current device: 2 forward work-groups per CU.
+int fwd_slots(int* slots) {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        return FA_ERR_LAUNCH;
+    *slots = 2 * cus;
+    return FA_OK;
+}
+
+// The persistent forward on a grid of about as many work-groups as the CUs hold
+// at once (a multiple of the 8 XCDs).
+int launch_fwd_persistent(const AttnParams& p, int d, int causal, int slots, hipStream_t s) {
+    const int64_t items = (int64_t)p.n_tiles * p.H * p.batch;
+    const int grid = (int)std::max<int64_t>(8, std::min<int64_t>((int64_t)slots / 8 * 8, (items + 7) / 8 * 8));
+    if (d == 64)
+        return causal ? launch(fa_fwd_persistent_kernel<64, true>, grid, 256, s, p)
+                      : launch(fa_fwd_persistent_kernel<64, false>, grid, 256, s, p);
+    return causal ? launch(fa_fwd_persistent_kernel<128, true>, grid, 256, s, p)
+                  : launch(fa_fwd_persistent_kernel<128, false>, grid, 256, s, p);
+}
+
 }  // namespace
 
 extern "C" {
@@ -275,52 +317,31 @@ int fa_version(void) { return kVersion; }
 
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq,
            int Nk, int d, float scale, int causal, void* stream) {
-    if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
-    if (B <= 0 || Nq <= 0 || Nk <= 0) return FA_ERR_SHAPE;
-    int st = check_common(H, d, scale, causal);
+    AttnParams p;
+    int st = prepare_fwd(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, &p);
     if (st) return st;
-    if (causal && Nq != Nk) return FA_ERR_UNSUPPORTED;
-    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
-        return FA_ERR_ALIGN;
-    const int ntq = (Nq + FwdCfg<128>::BM - 1) / FwdCfg<128>::BM;
-    st = check_sizes((int64_t)B * Nq, (int64_t)B * Nk, Nq, Nk, H, d, (int64_t)ntq * H * B);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    // A grid that fits in one round of work-group slots runs as the persistent
+    // kernel, whose deal pairs long causal tiles with short ones on each CU (the
+    // hardware's in-order dispatch gives some CUs two of the longest); larger
+    // grids balance themselves as work-groups finish, and the per-tile kernel
+    // is faster there.  Both compute every tile the same way (bitwise equal).
+    int slots = 0;
+    st = fwd_slots(&slots);
     if (st) return st;
-    AttnParams p = base_params(q, k, v, B, H, Nq, Nk, scale);
-    p.o = static_cast<bf16*>(o);
-    p.lse = lse;
-    p.n_tiles = ntq;
-    return launch_fwd<false>(p, d, causal, static_cast<hipStream_t>(stream));
+    if ((int64_t)p.n_tiles * H * B <= slots) return launch_fwd_persistent(p, d, causal, slots, s);
+    return launch_fwd<false>(p, d, causal, s);
 }
 
 int fa_fwd_persistent(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                       int Nq, int Nk, int d, float scale, int causal, void* stream) {
-    if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
-    if (B <= 0 || Nq <= 0 || Nk <= 0) return FA_ERR_SHAPE;
-    int st = check_common(H, d, scale, causal);
+    AttnParams p;
+    int st = prepare_fwd(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, &p);
     if (st) return st;
-    if (causal && Nq != Nk) return FA_ERR_UNSUPPORTED;
-    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
-        return FA_ERR_ALIGN;
-    const int ntq = (Nq + FwdCfg<128>::BM - 1) / FwdCfg<128>::BM;
-    st = check_sizes((int64_t)B * Nq, (int64_t)B * Nk, Nq, Nk, H, d, (int64_t)ntq * H * B);
+    int slots = 0;
+    st = fwd_slots(&slots);
     if (st) return st;
-    AttnParams p = base_params(q, k, v, B, H, Nq, Nk, scale);
-    p.o = static_cast<bf16*>(o);
-    p.lse = lse;
-    p.n_tiles = ntq;
-    // a grid the CUs hold at once (2 work-groups per CU), a multiple of the 8 XCDs
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-        return FA_ERR_LAUNCH;
-    const int64_t items = (int64_t)ntq * H * B;
-    const int grid = (int)std::max<int64_t>(8, std::min<int64_t>((int64_t)(2 * cus) / 8 * 8, (items + 7) / 8 * 8));
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    if (d == 64)
-        return causal ? launch(fa_fwd_persistent_kernel<64, true>, grid, 256, s, p)
-                      : launch(fa_fwd_persistent_kernel<64, false>, grid, 256, s, p);
-    return causal ? launch(fa_fwd_persistent_kernel<128, true>, grid, 256, s, p)
-                  : launch(fa_fwd_persistent_kernel<128, false>, grid, 256, s, p);
+    return launch_fwd_persistent(p, d, causal, slots, static_cast<hipStream_t>(stream));
 }
 
 int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
