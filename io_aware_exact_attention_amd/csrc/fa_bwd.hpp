@@ -18,7 +18,7 @@
 //   2. fa_bwd_dkdv_kernel: key-tile outer.  A work-group owns a 128-key tile
 //      (K rows in registers, 32 keys per wave; V in LDS) and keeps the dK^T,
 //      dV^T accumulators on chip, streams the query rows that can see those keys
-//      (Q, dO, LSE, D; double-buffered through LDS) and evaluates S, dP
+//      (Q, dO, LSE, D; double-buffered through LDS, from the last rows down) and evaluates S, dP
 //      (row-wise LDS operand reads) and dV^T += dO^T P, dK^T += Q^T dS
 //      (transposed LDS operand reads).
 //      S = Q K^T is computed with keys as the accumulator's columns, so each
@@ -181,11 +181,16 @@ void fa_bwd_dkdv_kernel(AttnParams p) {
     const uint32_t stat_bytes = (uint32_t)nq * 4;
     const int q_first = CAUSAL ? kv_start : 0;   // BN is a multiple of BMQ
     const int n_q = nq > q_first ? (nq - q_first + C::BMQ - 1) / C::BMQ : 0;
+    // Stages run from the last query rows down: every key tile of a head needs the
+    // last rows, so the work-groups of one head that start together read the same
+    // Q and dO rows at the same time and share them in the XCD's L2 (upward, each
+    // would start at its own first key, all at different rows).
+    auto stage_q0 = [&](int it) { return q_first + (n_q - 1 - it) * C::BMQ; };
     const TileLoader<D, C::BMQ, C::NW> qload(row_bytes, wave, lane);
 
     auto issue = [&](int it) {
         FA_LDS char* st = lds + C::STAGE0 + (it & 1) * 2 * C::TILE_BYTES;
-        const int q0 = q_first + it * C::BMQ;
+        const int q0 = stage_q0(it);
         qload.load(st, qbase, q_bytes, q0 * row_bytes, wave);
         qload.load(st + C::TILE_BYTES, gbase, q_bytes, q0 * row_bytes, wave);
         FA_LDS char* sd = lds + C::STATS0 + (it & 1) * C::STAT_BYTES;
@@ -205,7 +210,7 @@ void fa_bwd_dkdv_kernel(AttnParams p) {
         wait_vmem();
         __syncthreads();
         if (it + 1 < n_q) issue(it + 1);
-        const int q0 = q_first + it * C::BMQ;
+        const int q0 = stage_q0(it);
         if (CAUSAL && q0 + 31 < kw0) return;   // every query here precedes every key
 
         // S = Q K^T and dP - D = dO V^T - D: rows are queries (this lane's rows are
