@@ -104,6 +104,10 @@ def parse():
     ap.add_argument("--forward", choices=("tiles", "persistent"), default="tiles",
                     help="forward kernel of the dense step: one work-group per tile (fa_fwd) or the "
                          "persistent longest-first kernel (fa_fwd_persistent)")
+    ap.add_argument("--max-seqlen", type=int, default=0,
+                    help="packed workloads: max_seqlen passed to the kernels (default: the longest "
+                         "sequence; a larger value adds only work-groups that find no rows, which "
+                         "measures what the grid's empty work-groups cost)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="wall-time budget of the CPU oracle sample (0 disables it)")
     return ap.parse_args()
@@ -388,7 +392,7 @@ def run_varlen(args, w):
     x = wl.make_inputs(w.name)
     q, k, v, do = (x[n].to(dev) for n in ("q", "k", "v", "dout"))
     cu = x["cu_seqlens"].to(dev)
-    mx = x["max_seqlen"]
+    mx = max(x["max_seqlen"], args.max_seqlen)
     nseq = cu.numel() - 1
     causal = w.causal[-1]
     o = torch.empty_like(q)
