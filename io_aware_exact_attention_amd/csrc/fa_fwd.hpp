@@ -2,13 +2,17 @@
 //
 // Method ("08 · FlashAttention", §二; "LLM Systems 22: Flash Attention", §3.1):
 // each work-group owns a tile of BM query rows and streams the key/value rows in
-// tiles of BN.  Per query row it keeps a running maximum m, a running sum l and an
+// tiles of BN.  Per query row it keeps a reference maximum m, a running sum l and an
 // unnormalised accumulator O; a new tile with scores S' updates them as
-//     m_new = max(m, rowmax S'),  P~ = exp(S' - m_new),
+//     m_new = rowmax S' if that exceeds m by more than 2 ln 2, else m,
+//     P~ = exp(S' - m_new),
 //     l <- e^(m - m_new) l + rowsum P~,   O <- e^(m - m_new) O + P~ V',
-// and O / l is written once at the end with LSE = m + ln l.  (Here P~ is rounded
-// to bf16 for the P V product; O is divided by the sum of those rounded values,
-// LSE uses the unrounded l.)  Work is done in the
+// and O / l is written once at the end with LSE = m + ln l.  Any m at or below
+// the true maximum gives the same result; keeping m unless the maximum rises
+// by a factor above 4 ("LLM Systems 22: Flash Attention", §4.2.1: the online
+// softmax that skips most rescaling) leaves P~ <= 4 and lets a wave skip O's
+// rescale on most tiles.  (P~ is rounded to bf16 for the P V product; O is
+// divided by the sum of those rounded values, LSE uses the unrounded l.)  Work is done in the
 // base-2 domain: exp(x*scale) = exp2(x * scale*log2 e), the scale folded into
 // one FMA per score.  With the causal mask only key tiles at or below the
 // diagonal are visited, and only tiles that straddle it are masked.
@@ -47,6 +51,8 @@ struct FwdCfg {
     static constexpr int DBLK = D / 32;          // 32-wide blocks of the head dim
     static constexpr int KB = BN / 32;           // 32-key blocks per tile
     static constexpr int LDS_BYTES = 2 * 2 * TILE_BYTES;   // [buffer][K | V]
+    // the online softmax's reference maximum moves only on a rise above 2^2 (exp2 units)
+    static constexpr float RESCALE_LOG2 = 2.f;
 };
 
 // One work item: query tile `tile` of (batch or sequence, head) pair `bh`, with
@@ -101,7 +107,7 @@ __device__ __forceinline__ void fwd_tile(const AttnParams& p, char* smem, int bh
     for (int cb = 0; cb < C::DBLK; ++cb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[cb][r] = 0.f;
-    float m = kNegInf;   // running max of raw scores q.k (this row)
+    float m = kNegInf;   // reference maximum of raw scores q.k (this row)
     float l = 0.f;       // running sum, over the keys this lane holds (gives LSE)
     float lr = 0.f;      // the same sum of the bf16-rounded P~ that the P V product uses
     float alpha = 0.f;   // e^(m_old - m) of the tile whose scores are held
@@ -152,7 +158,10 @@ __device__ __forceinline__ void fwd_tile(const AttnParams& p, char* smem, int bh
 #pragma unroll
             for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb][r]);
         mx = max_halves(mx);
-        const float m_new = fmaxf(m, mx);
+        // the reference moves only when the tile's maximum exceeds it by more than
+        // RESCALE_LOG2 in exp2 units, so P~ <= 2^RESCALE_LOG2; otherwise it stays and
+        // alpha = 1 (a first finite maximum always moves it from -inf)
+        const float m_new = (mx * c > m * c + C::RESCALE_LOG2) ? mx : m;
         const float m_ref = (m_new == kNegInf) ? 0.f : m_new;
         alpha = fast_exp2((m - m_ref) * c);
         mc = m_ref * c;
@@ -186,13 +195,11 @@ __device__ __forceinline__ void fwd_tile(const AttnParams& p, char* smem, int bh
         }
         lr = rr;
     };
-    // O^T[dim][query] = alpha O^T + V^T P^T; V^T operand via transposed LDS reads
+    // O^T[dim][query] += V^T P^T; V^T operand via transposed LDS reads
     // of the same key order: rows 16*ks + 4*h2 + 0..3 and +8
     auto pv = [&](const FA_LDS char* vt, const bf16x8 (&pk)[C::BN / 16]) __attribute__((always_inline)) {
 #pragma unroll
         for (int cb = 0; cb < C::DBLK; ++cb) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[cb][r] *= alpha;
 #pragma unroll
             for (int ks2 = 0; ks2 < C::BN / 16; ++ks2) {
                 const int c0 = cb * 32 + 16 * g;
@@ -227,10 +234,17 @@ __device__ __forceinline__ void fwd_tile(const AttnParams& p, char* smem, int bh
             loader.load(ldsb + (1 - PB) * 2 * C::TILE_BYTES + C::TILE_BYTES, vbase, kv_bytes,
                         (t + 1) * C::BN * row_bytes, wave_s);
         if (t >= n_w) return;
-        // one basic block per case (the compiler interleaves its products with its
-        // vector work only within a block).  O's rescale is unconditional: under
-        // the causal mask of B8 H16 N4096 some row of a 32-row wave moves its
-        // maximum in 78% of tiles, and its multiplies sit among the products.
+        // O's rescale for tile t, only when some row of the wave moved its reference
+        // (26% of the wave-tiles of B8 H16 N4096 causal, against 78% with a
+        // reference that follows every new maximum)
+        if (wave_any(alpha != 1.f)) {
+#pragma unroll
+            for (int cb = 0; cb < C::DBLK; ++cb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[cb][r] *= alpha;
+        }
+        // one basic block per case: the compiler interleaves its products with its
+        // vector work only within a block
         auto full = [&](auto masked) __attribute__((always_inline)) {
             bf16x8 pk[C::BN / 16];
             f32x16 sn[C::KB];
