@@ -290,10 +290,10 @@ int launch_fwd_persistent(const AttnParams& p, int d, int causal, int slots, hip
     const int64_t items = (int64_t)p.n_tiles * p.H * p.batch;
     const int grid = (int)std::max<int64_t>(8, std::min<int64_t>((int64_t)slots / 8 * 8, (items + 7) / 8 * 8));
     if (d == 64)
-        return causal ? launch(fa_fwd_persistent_kernel<64, true>, grid, 256, s, p)
-                      : launch(fa_fwd_persistent_kernel<64, false>, grid, 256, s, p);
-    return causal ? launch(fa_fwd_persistent_kernel<128, true>, grid, 256, s, p)
-                  : launch(fa_fwd_persistent_kernel<128, false>, grid, 256, s, p);
+        return causal ? launch(fa_fwd_persistent_kernel<64, true>, grid, FwdCfg<64>::NW * 64, s, p)
+                      : launch(fa_fwd_persistent_kernel<64, false>, grid, FwdCfg<64>::NW * 64, s, p);
+    return causal ? launch(fa_fwd_persistent_kernel<128, true>, grid, FwdCfg<128>::NW * 64, s, p)
+                  : launch(fa_fwd_persistent_kernel<128, false>, grid, FwdCfg<128>::NW * 64, s, p);
 }
 
 }  // namespace

@@ -96,7 +96,15 @@ __device__ __forceinline__ void fwd_tile(const AttnParams& p, char* smem, int bh
     // this wave's key tiles: under the causal mask the ones that start at or
     // before its last row.  Only the last of them can need a mask (the diagonal
     // tile, or the ragged tail of the keys).
-    const int n_w = CAUSAL ? min(n_kv, (qw0 + 31) / C::BN + 1) : n_kv;
+    int n_w = CAUSAL ? min(n_kv, (qw0 + 31) / C::BN + 1) : n_kv;
+    // An empty asm hides the count from the optimiser, as the causal count
+    // already is (it depends on the wave).  When it can prove the loop's tile
+    // cases uniform (the non-causal n_w is the work-group's n_kv), the ROCm 7.2
+    // compiler schedules across their branches and runs out of registers: the
+    // d = 128 non-causal kernel spilled 232 bytes per lane to scratch and took
+    // 1.90 ms on B8 H16 N4096 instead of 1.10 ms.  Behind the asm every forward
+    // variant fits in 223 registers with no scratch.
+    asm volatile("" : "+v"(n_w));
     const bf16* qptr = p.q + (int64_t)(qs + min(qi, nq - 1)) * tok + h * D + 8 * h2;
     bf16x8 qf[C::KSTEPS];
 #pragma unroll
