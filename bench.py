@@ -546,8 +546,11 @@ def main():
     fwd_tf = f_fwd / (t_fwd * 1e-3) / 1e12
     fb_tf_events = (f_fwd + f_bwd) / ((t_fwd + t_bwd) * 1e-3) / 1e12
     value = (f_fwd + f_bwd) / wall / 1e12
+    shape = f"B{B} H{H} N{N} d{d} {'causal' if causal else 'non-causal'}"
+    if w.k_scale != 1.0:
+        shape += f", K x{w.k_scale:g}"
     out = {
-        "metric": METRIC,
+        "metric": METRIC.replace("B8 H16 N4096 d128 causal", shape),
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
