@@ -414,60 +414,98 @@ void fa_bwd_dq_kernel(AttnParams p) {
         const int kv0 = t * C::BN;
         if (CAUSAL && kv0 > qw0 + 31) return;
 
-        // S^T = K Q^T, dP^T = V dO^T: rows keys, columns this wave's queries
-        f32x16 sT[C::KB], dpT[C::KB];
+        // The tile in 32-key halves, each through S, dS and its dQ products before
+        // the next: half the score registers of a whole-tile pass, which leaves
+        // the compiler room to read K and V operands ahead of their products.
+        // The accumulation order of every product is that of a whole-tile pass.
+        auto body = [&](auto masked) __attribute__((always_inline)) {
 #pragma unroll
-        for (int kb = 0; kb < C::KB; ++kb) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                sT[kb][r] = 0.f;
-                dpT[kb][r] = 0.f;
-            }
-            const int row = kb * 32 + col;
-#pragma unroll
-            for (int k2 = 0; k2 < C::KSTEPS; ++k2) {
-                const int off = tile_off<D>(row, 2 * k2 + h2);
-                sT[kb] = mfma_32x32x16(lds_read16(kt + off), qf[k2], sT[kb]);
-                dpT[kb] = mfma_32x32x16(lds_read16(vt + off), gf[k2], dpT[kb]);
-            }
-        }
-        // masked scores become -inf so that their P is exactly 0
-        if ((CAUSAL && kv0 + C::BN - 1 > qw0) || (kv0 + C::BN > nk)) {
-#pragma unroll
-            for (int kb = 0; kb < C::KB; ++kb)
+            for (int kb = 0; kb < C::KB; ++kb) {
+                // S^T = K Q^T, dP^T = V dO^T: rows keys, columns this wave's queries
+                f32x16 sT, dpT;
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int kj = kv0 + kb * 32 + 8 * (r >> 2) + 4 * h2 + (r & 3);
-                    if ((CAUSAL && kj > qi) || kj >= nk) sT[kb][r] = kNegInf;
+                    sT[r] = 0.f;
+                    dpT[r] = 0.f;
                 }
-        }
+                const int row = kb * 32 + col;
 #pragma unroll
-        for (int kb = 0; kb < C::KB; ++kb)
+                for (int k2 = 0; k2 < C::KSTEPS; ++k2) {
+                    const int off = tile_off<D>(row, 2 * k2 + h2);
+                    sT = mfma_32x32x16(lds_read16(kt + off), qf[k2], sT);
+                    dpT = mfma_32x32x16(lds_read16(vt + off), gf[k2], dpT);
+                }
+                // masked scores become -inf so that their P is exactly 0
+                if constexpr (decltype(masked)::value) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float pr = fast_exp2(__builtin_fmaf(sT[kb][r], c, -lse2));
-                sT[kb][r] = pr * (dpT[kb][r] + nd);   // dS^T
+                    for (int r = 0; r < 16; ++r) {
+                        const int kj = kv0 + kb * 32 + 8 * (r >> 2) + 4 * h2 + (r & 3);
+                        if ((CAUSAL && kj > qi) || kj >= nk) sT[r] = kNegInf;
+                    }
+                }
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const float pr = fast_exp2(__builtin_fmaf(sT[r], c, -lse2));
+                    sT[r] = pr * (dpT[r] + nd);   // dS^T
+                }
+                bf16x8 dsk[2];
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    float tmp[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) tmp[e] = sT[8 * hh + e];
+                    dsk[hh] = pack8(tmp);
+                }
+                // dQ^T[dim][query] += K^T dS^T over this half's keys, K^T via
+                // transposed LDS reads
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    const int k2 = 2 * kb + hh;
+#pragma unroll
+                    for (int cb = 0; cb < C::DBLK; ++cb) {
+                        const int c0 = cb * 32 + 16 * g;
+                        const int rk = k2 * 16 * C::ROW_BYTES;   // 16 more rows keep the swizzle
+                        const bf16x8 a = join(lds_read_tr(kt + tr_off<D>(4 * h2, c0, sl) + rk),
+                                              lds_read_tr(kt + tr_off<D>(4 * h2 + 8, c0, sl) + rk));
+                        acc[cb] = mfma_32x32x16(a, dsk[hh], acc[cb]);
+                    }
+                }
             }
-        bf16x8 dsk[C::BN / 16];
+            // Read-ahead: the compiler's own schedule issues each K / V operand
+            // read one product before its use and waits for it; these groups keep
+            // about four reads in flight.  Per half: 4 reads, then pairs of S / dP
+            // products each followed by the reads two products ahead, then the dQ
+            // products interleaved with their transposed reads.
 #pragma unroll
-        for (int k2 = 0; k2 < C::BN / 16; ++k2) {
-            float tmp[8];
+            for (int kb = 0; kb < C::KB; ++kb) {
+                __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);   // 0x100: LDS reads
 #pragma unroll
-            for (int e = 0; e < 8; ++e) tmp[e] = sT[k2 >> 1][8 * (k2 & 1) + e];
-            dsk[k2] = pack8(tmp);
-        }
-        // dQ^T[dim][query] += K^T dS^T, K^T via transposed LDS reads
+                for (int i = 0; i < C::KSTEPS - 2; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // 0x008: MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                }
+                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
-        for (int k2 = 0; k2 < C::BN / 16; ++k2) {
-#pragma unroll
-            for (int cb = 0; cb < C::DBLK; ++cb) {
-                const int c0 = cb * 32 + 16 * g;
-                const int rk = k2 * 16 * C::ROW_BYTES;   // 16 more rows keep the swizzle
-                const bf16x8 a = join(lds_read_tr(kt + tr_off<D>(4 * h2, c0, sl) + rk),
-                                      lds_read_tr(kt + tr_off<D>(4 * h2 + 8, c0, sl) + rk));
-                acc[cb] = mfma_32x32x16(a, dsk[k2], acc[cb]);
+                for (int i = 0; i < 2 * C::DBLK - 2; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                }
+                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
             }
-        }
+        };
+        // only the diagonal tile and a ragged tail take the masked copy.  The
+        // test is hidden from the optimiser (as the forward's tile count is):
+        // proven wave-uniform, it lets the compiler schedule across the two
+        // copies, and the d = 128 non-causal kernel then spills to scratch
+        int masked = (CAUSAL && kv0 + C::BN - 1 > qw0) || (kv0 + C::BN > nk);
+        asm volatile("" : "+v"(masked));
+        if (masked)
+            body(std::true_type{});
+        else
+            body(std::false_type{});
     };
     for (int t = 0; t < n_kv; t += 2) {   // two tiles per trip: buffer offsets are constants
         step(t, std::integral_constant<int, 0>{});
