@@ -72,10 +72,16 @@ int fa_version(void);
  *   lse [B,H,Nq] fp32 (written)
  *   scale: multiplies Q K^T (1/sqrt(d) for standard attention); must be finite and > 0.
  *   causal: 0 or 1.
- * When the query tiles (128 rows) of all (batch, head) pairs fit on the GPU at
- * once (two work-groups per CU), this runs fa_fwd_persistent's kernel, whose
- * longest-first deal balances a single round better than dispatch order does;
- * otherwise one work-group per query tile.  The results are the same bit for bit.
+ * Kernel choice (every choice computes the same O and LSE within rounding):
+ *   - causal, with at most one query tile (128 rows) of all (batch, head) pairs
+ *     per CU, or at most two per CU and at least 16 tiles per sequence: the
+ *     key-split kernel, one 8-wave work-group per query tile whose two halves
+ *     of waves take half of the tile's key tiles each and merge their running
+ *     (max, sum, O) through LDS ("LLM Systems 22: Flash Attention", §4.1.5
+ *     load balancing: the longest tile's chain of key tiles is halved);
+ *   - otherwise, when the tiles fit on the GPU at once (two work-groups per
+ *     CU): fa_fwd_persistent's kernel (bitwise the per-tile kernel's results);
+ *   - otherwise one work-group per query tile.
  */
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            int B, int H, int Nq, int Nk, int d, float scale, int causal, void* stream);
@@ -87,7 +93,8 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
  * hold at once loops over the query tiles, taken longest first (every pair's
  * tile with the most causal keys, then the next, ...), each XCD working on its
  * own (batch, head) pairs.  Arguments, results and errors as fa_fwd; the
- * outputs are bitwise those of fa_fwd (the same tile computation).
+ * outputs are bitwise those of fa_fwd wherever fa_fwd does not take the
+ * key-split kernel (the same tile computation).
  */
 int fa_fwd_persistent(const void* q, const void* k, const void* v, void* o, float* lse,
                       int B, int H, int Nq, int Nk, int d, float scale, int causal, void* stream);

@@ -64,11 +64,20 @@ struct FwdCfg {
 // vector unit busy at once instead of alternating between them.  K tiles and V
 // tiles therefore live one tile apart in two double buffers: when iteration t
 // starts, K(t+1) and V(t) are in LDS and the loads of K(t+2) and V(t+1) go out.
-template <int D, bool CAUSAL, bool VARLEN>
+//
+// SPLIT = 2 (key-split form, 8 waves): waves 0-3 take the first ceil(n/2) of the
+// work-group's n key tiles and waves 4-7 the rest, each half with its own LDS
+// buffers; both halves run the same number of barriers.  At the end the second
+// half's (m, l, lr, O) go through LDS to the wave of the first half that holds the
+// same query rows, which combines the two online-softmax states exactly as a new
+// tile would (scale each by e^(m_half - m_max), add) and writes the output.
+template <int D, bool CAUSAL, bool VARLEN, int SPLIT = 1>
 __device__ __forceinline__ void fwd_tile(const AttnParams& p, char* smem, int bh, int tile) {
     using C = FwdCfg<D>;
+    static_assert(SPLIT == 1 || SPLIT == 2, "one or two key halves");
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = (threadIdx.x >> 6) & (C::NW - 1);   // row block of this wave
+    const int half = SPLIT == 2 ? (threadIdx.x >> 6) / C::NW : 0;
     const int h2 = lane >> 5;
     const int col = lane & 31;
     const int sl = lane & 15;
@@ -81,14 +90,23 @@ __device__ __forceinline__ void fwd_tile(const AttnParams& p, char* smem, int bh
     const int q_start = tile * C::BM;
     if (q_start >= nq) return;
     const int kv_end = CAUSAL ? min(nk, q_start + C::BM) : nk;
-    const int n_kv = (kv_end + C::BN - 1) / C::BN;   // the work-group's key tiles
+    const int n_all = (kv_end + C::BN - 1) / C::BN;   // the work-group's key tiles
+    // this half's key tiles [kt0, kt0 + n_kv), and the loop's trip count (the same
+    // for every wave of the work-group: each trip has one barrier)
+    const int n_first = SPLIT == 2 ? (n_all + 1) / 2 : n_all;
+    const int kt0 = half ? n_first : 0;
+    const int n_kv = half ? n_all - n_first : n_first;
+    const int n_iter = n_first;
     const int64_t tok = (int64_t)p.H * D;
-    const bf16* kbase = p.k + (int64_t)ks * tok + h * D;
-    const bf16* vbase = p.v + (int64_t)ks * tok + h * D;
     const int row_bytes = p.H * D * 2;
-    const uint32_t kv_bytes = (uint32_t)nk * row_bytes;
+    // this half's keys start at row kt0 * BN (at most nk: an empty second half
+    // issues no loads)
+    const int k_first = min(kt0 * C::BN, nk);
+    const bf16* kbase = p.k + (int64_t)(ks + k_first) * tok + h * D;
+    const bf16* vbase = p.v + (int64_t)(ks + k_first) * tok + h * D;
+    const uint32_t kv_bytes = (uint32_t)(nk - k_first) * row_bytes;
     const TileLoader<D, C::BN, C::NW> loader(row_bytes, wave, lane);
-    FA_LDS char* ldsb = (FA_LDS char*)smem;
+    FA_LDS char* ldsb = (FA_LDS char*)smem + half * C::LDS_BYTES;
     const int wave_s = __builtin_amdgcn_readfirstlane(wave);   // LDS destinations are wave-uniform
 
     const int qw0 = q_start + wave * 32;   // first query row of this wave
@@ -96,7 +114,11 @@ __device__ __forceinline__ void fwd_tile(const AttnParams& p, char* smem, int bh
     // this wave's key tiles: under the causal mask the ones that start at or
     // before its last row.  Only the last of them can need a mask (the diagonal
     // tile, or the ragged tail of the keys).
-    int n_w = CAUSAL ? min(n_kv, (qw0 + 31) / C::BN + 1) : n_kv;
+    // (In the key-split form, the last tile of the first half is masked too when
+    // the wave's range continues in the second half; such a tile lies wholly
+    // below the wave's first row and within the keys, so the mask leaves it as is.)
+    int n_w = CAUSAL ? min(n_all, (qw0 + 31) / C::BN + 1) : n_all;
+    n_w = min(max(n_w - kt0, 0), n_kv);
     // An empty asm hides the count from the optimiser, as the causal count
     // already is (it depends on the wave).  When it can prove the loop's tile
     // cases uniform (the non-causal n_w is the work-group's n_kv), the ROCm 7.2
@@ -149,7 +171,7 @@ __device__ __forceinline__ void fwd_tile(const AttnParams& p, char* smem, int bh
     };
     // causal diagonal / ragged tail of key tile t
     auto mask = [&](f32x16 (&sc)[C::KB], int t) __attribute__((always_inline)) {
-        const int kv0 = t * C::BN;
+        const int kv0 = (kt0 + t) * C::BN;
 #pragma unroll
         for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
@@ -274,9 +296,41 @@ __device__ __forceinline__ void fwd_tile(const AttnParams& p, char* smem, int bh
             pv(v_cur, pk);
         }
     };
-    for (int t = 0; t < n_kv; t += 2) {
+    for (int t = 0; t < n_iter; t += 2) {
         iter(t, std::integral_constant<int, 0>{});
-        if (t + 1 < n_kv) iter(t + 1, std::integral_constant<int, 1>{});
+        if (t + 1 < n_iter) iter(t + 1, std::integral_constant<int, 1>{});
+    }
+
+    if constexpr (SPLIT == 2) {
+        // merge area [row block][value][lane] (fp32): O's 16 * DBLK accumulators,
+        // then m, l, lr -- written by the second half, read by the first
+        constexpr int NV = 16 * C::DBLK + 3;
+        static_assert(C::NW * NV * 64 * 4 <= 2 * C::LDS_BYTES, "merge area fits the K/V buffers");
+        FA_LDS float* mx = (FA_LDS float*)smem + wave * NV * 64 + lane;
+        __syncthreads();   // every wave is done with its K/V buffers
+        if (half == 1) {
+#pragma unroll
+            for (int cb = 0; cb < C::DBLK; ++cb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) mx[(cb * 16 + r) * 64] = acc[cb][r];
+            mx[(NV - 3) * 64] = m;
+            mx[(NV - 2) * 64] = l;
+            mx[(NV - 1) * 64] = lr;
+        }
+        __syncthreads();
+        if (half == 1) return;
+        const float m1 = mx[(NV - 3) * 64];
+        const float mm = fmaxf(m, m1);
+        const float m_ref = (mm == kNegInf) ? 0.f : mm;
+        const float a0 = fast_exp2((m - m_ref) * c);
+        const float a1 = fast_exp2((m1 - m_ref) * c);
+        l = l * a0 + mx[(NV - 2) * 64] * a1;
+        lr = lr * a0 + mx[(NV - 1) * 64] * a1;
+#pragma unroll
+        for (int cb = 0; cb < C::DBLK; ++cb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[cb][r] = acc[cb][r] * a0 + mx[(cb * 16 + r) * 64] * a1;
+        m = mm;
     }
 
     const float lt = sum_halves(l);
@@ -307,6 +361,21 @@ void fa_fwd_kernel(AttnParams p) {
     int bh, rank;
     xcd_work_item(blockIdx.x, p.n_tiles, p.H * p.batch, bh, rank);
     fwd_tile<D, CAUSAL, VARLEN>(p, smem, bh, p.n_tiles - 1 - rank);   // longest causal rows first
+}
+
+// Key-split form for grids that fill at most one round of the CUs' work-group
+// slots (short causal sequences, few heads): one 8-wave work-group per query
+// tile, each half of its waves taking half of the tile's key tiles, so the
+// longest tile's chain of key tiles is halved.  Tiles are numbered longest
+// first (lpt_work_item); with one such work-group per CU, the hardware hands
+// the shorter tiles of the second round to the CUs that finish first.
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void fa_fwd_split_kernel(AttnParams p) {
+    __shared__ __attribute__((aligned(1024))) char smem[2 * FwdCfg<D>::LDS_BYTES];
+    int bh, rank;
+    lpt_work_item(blockIdx.x, p.n_tiles, p.H * p.batch, bh, rank);
+    fwd_tile<D, CAUSAL, false, 2>(p, smem, bh, p.n_tiles - 1 - rank);
 }
 
 // Persistent form ("LLM Systems 22: Flash Attention", §4.1.4 persistent kernels,

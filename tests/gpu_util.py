@@ -86,6 +86,18 @@ def check_grads(gpu, ref, what=""):
     return out
 
 
+def fwd_is_key_split(B, H, Nq, causal) -> bool:
+    """Whether fa_fwd runs the key-split kernel for this shape: causal grids of
+    128-row query tiles with at most one tile per CU, or with at most two per CU
+    and at least 16 tiles per sequence.  Its sums over the two key halves are
+    added in another order than the per-tile and persistent kernels', so its
+    output is not bitwise theirs."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    n_tiles = -(-Nq // 128)
+    items = n_tiles * B * H
+    return bool(causal) and (items <= cus or (items <= 2 * cus and n_tiles >= 16))
+
+
 def run_dense(x, scale, causal, backward=True):
     """x: dict of CPU bf16 tensors q, k, v (dout); returns GPU results on the host."""
     dev = torch.device("cuda", 0)

@@ -1,6 +1,8 @@
 """The persistent, longest-first forward (fa_fwd_persistent) on the GPU: bitwise
-equal to fa_fwd (each tile is the same computation, only the work-group that runs
-it differs) and, through that, to the oracle within the forward's bounds."""
+equal to fa_fwd wherever fa_fwd runs the per-tile or persistent kernel (each tile
+is the same computation, only the work-group that runs it differs), and to the
+oracle within the forward's bounds.  Small causal grids, where fa_fwd runs the
+key-split kernel instead, are compared with the oracle directly."""
 
 import pytest
 import torch
@@ -36,7 +38,8 @@ def test_persistent_equals_fa_fwd(case):
     o2, l2 = torch.empty_like(o1), torch.empty_like(l1)
     fa355.fa_fwd_persistent(q, k, v, o2, l2, scale, causal)
     torch.cuda.synchronize()
-    assert torch.equal(o1, o2) and torch.equal(l1, l2)
-    if B * N * Nk * H <= 2 * 300 * 300 * 8:
+    if not gu.fwd_is_key_split(B, H, N, causal):
+        assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    if B * N * Nk * H <= 2 * 300 * 300 * 8 or gu.fwd_is_key_split(B, H, N, causal):
         o_ref, l_ref = oracle.attention_forward(x["q"], x["k"], x["v"], scale, causal)
         gu.check_forward(o2, l2, o_ref, l_ref, f"persistent {case}")
