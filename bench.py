@@ -456,6 +456,78 @@ def run_varlen(args, w):
     print(json.dumps(out), flush=True)
 
 
+def fa_fwd_kernel_name(B: int, H: int, N: int, causal: bool) -> str:
+    """The kernel fa_fwd launches for a dense shape (its documented choice): the
+    key-split kernel for causal grids of at most one 128-row query tile per CU (or
+    two per CU with at least 16 tiles per sequence), else the persistent kernel
+    when the tiles fit two per CU, else one work-group per tile."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    n_tiles = -(-N // 128)
+    items = n_tiles * B * H
+    if causal and (items <= cus or (items <= 2 * cus and n_tiles >= 16)):
+        return "fa_fwd_split_kernel"
+    if items <= 2 * cus:
+        return "fa_fwd_persistent_kernel"
+    return "fa_fwd_kernel"
+
+
+def fa_bwd_is_fused(B: int, H: int, N: int, causal: bool) -> bool:
+    """Whether fa_bwd runs as the row-dot kernel and one launch holding both
+    passes (its documented choice for small dense grids: at most 8 causal or 2
+    non-causal dK/dV plus dQ work items of 128 rows per CU)."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    return 2 * (-(-N // 128)) * B * H <= (8 if causal else 2) * cus
+
+
+def small_config_rates(name: str, causal: bool, steps: int = 50, warmup: int = 10) -> dict:
+    """Forward and forward + backward rates of a small dense workload (one that is
+    launch- or tail-bound rather than MFMA-bound), timed like the main step with
+    HIP events over `steps` back-to-back steps after `warmup` untimed ones."""
+    w = wl.WORKLOADS[name]
+    dev = torch.device("cuda", 0)
+    x = wl.make_inputs(w.name)
+    q, k, v, do = (x[n].to(dev) for n in ("q", "k", "v", "dout"))
+    B, N, H, d = q.shape
+    o = torch.empty_like(q)
+    lse = torch.empty(B, H, N, dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(fa355.fa_bwd_workspace_bytes(B, H, N, d) // 4, dtype=torch.float32, device=dev)
+    calls = [
+        lambda: fa355.fa_fwd(q, k, v, o, lse, w.scale, causal),
+        lambda: fa355.fa_bwd(q, k, v, o, do, lse, dq, dk, dv, ws, w.scale, causal),
+    ]
+    for _ in range(warmup):
+        for c in calls:
+            c()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    for s in range(steps):
+        ev[s][0].record()
+        calls[0]()
+        ev[s][1].record()
+        for c in calls[1:]:
+            c()
+    torch.cuda.synchronize()
+    t_fwd = sorted(e0.elapsed_time(e1) for e0, e1 in ev)
+    e_start, e_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e_start.record()
+    for _ in range(steps):
+        for c in calls:
+            c()
+    e_end.record()
+    torch.cuda.synchronize()
+    t_step = e_start.elapsed_time(e_end) / steps
+    cnt = acc.dense_counts(B, H, N, d, causal)
+    fwd_ms = sum(t_fwd) / len(t_fwd)
+    fwd_tf = cnt["flops_fwd"] / (fwd_ms * 1e-3) / 1e12
+    step_tf = (cnt["flops_fwd"] + cnt["flops_bwd"]) / (t_step * 1e-3) / 1e12
+    return {"shape": f"B{B} H{H} N{N} d{d} {'causal' if causal else 'non-causal'}",
+            "fwd_ms": round(fwd_ms, 5), "fwd_ms_min": round(t_fwd[0], 5),
+            "fwd_tflops": round(fwd_tf, 2), "fwd_pct_peak": round(100 * fwd_tf / PEAK_BF16_TFLOPS, 2),
+            "step_ms": round(t_step, 5), "fwd_bwd_tflops": round(step_tf, 2),
+            "fwd_bwd_pct_peak": round(100 * step_tf / PEAK_BF16_TFLOPS, 2)}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -484,14 +556,18 @@ def main():
     scale = w.scale
 
     persistent = args.forward == "persistent"
-    names = ["fa_fwd_persistent_kernel" if persistent else "fa_fwd_kernel", "fa_bwd_dq_kernel",
-             "fa_bwd_dkdv_kernel"]
+    fused = fa_bwd_is_fused(B, H, N, causal)
+    names = ["fa_fwd_persistent_kernel" if persistent else fa_fwd_kernel_name(B, H, N, causal),
+             "fa_bwd_dq_kernel", "fa_bwd_dkdv_kernel"]
     fwd = fa355.fa_fwd_persistent if persistent else fa355.fa_fwd
     calls = [   # fa_bwd = fa_bwd_dq_dot, then fa_bwd_dkdv (one kernel each)
         lambda: fwd(q, k, v, o, lse, scale, causal),
         lambda: fa355.fa_bwd_dq_dot(q, k, v, o, do, lse, ws, dq, scale, causal),
         lambda: fa355.fa_bwd_dkdv(q, k, v, do, ws, dk, dv, scale, causal),
     ]
+    if fused:   # small grids: fa_bwd is the row-dot kernel, then both passes in one launch
+        names = names[:1] + ["fa_bwd_dot_kernel + fa_bwd_fused_kernel"]
+        calls = calls[:1] + [lambda: fa355.fa_bwd(q, k, v, o, do, lse, dq, dk, dv, ws, scale, causal)]
     calibration_copy(dev)
 
     for _ in range(args.warmup):
@@ -518,7 +594,7 @@ def main():
     pairs = cnt["pairs"]
     f_fwd, f_bwd = cnt["flops_fwd"], cnt["flops_bwd"]
     # algorithmic FLOPs attributed per kernel (the 10d backward = 2d in dQ + 8d in dK/dV)
-    kern_flops = [f_fwd, 2 * d * pairs, 8 * d * pairs]
+    kern_flops = [f_fwd, 2 * d * pairs, 8 * d * pairs] if not fused else [f_fwd, 10 * d * pairs]
     kern = {}
     for n, ms, fl, ts in zip(names, kern_ms, kern_flops, per_step):
         ts = sorted(ts)
@@ -530,6 +606,9 @@ def main():
     tok = B * N * H
     kern_bytes = [cnt["bytes_fwd"], tok * (5 * 2 * d + 4) + tok * (2 * d + 8),
                   tok * (4 * 2 * d + 8) + tok * 2 * 2 * d]
+    if fused:   # the row-dot kernel (o, dout, LSE in; -D, LSE*log2(e) out), then both passes
+        # and both passes together (q, k, v, dout, -D, LSE*log2(e) in; dq, dk, dv out)
+        kern_bytes = [kern_bytes[0], tok * (2 * 2 * d + 4 + 8) + tok * (4 * 2 * d + 8) + tok * 3 * 2 * d]
     traffic = measured_traffic(w.name)
     dom = max(range(len(names)), key=lambda i: kern_ms[i])
     achieved = kern_flops[dom] / (kern_ms[dom] * 1e-3) / 1e12
@@ -573,6 +652,14 @@ def main():
         "roofline": roof,
         "device": torch.cuda.get_device_name(0),
     }
+    if w.name == wl.HEADLINE:
+        # the small configurations, after the timed region: launch- and tail-bound
+        # shapes whose rates the headline line would not show
+        out["small_configs"] = {
+            "tiny": small_config_rates("tiny", False),
+            "b4_h16_n1024_d64_causal": small_config_rates("b4_h16_n1024_d64", True),
+            "b4_h16_n1024_d64_noncausal": small_config_rates("b4_h16_n1024_d64", False),
+        }
     if args.cpu_seconds > 0:
         xc = {n: x[n] for n in ("q", "k", "v", "dout")}
         out["cpu_baseline"] = cpu_baseline(xc, w, causal, args.cpu_seconds)

@@ -1,9 +1,11 @@
 // A C++ caller of libfa355 through the C ABI alone (no Python, no torch): it
 // allocates device buffers with the HIP runtime, runs the forward (per-tile and
 // persistent), the backward and a decoding call on a small seeded problem, and
-// checks what needs no reference implementation: the two forwards agree bit for
-// bit, row 0 of a causal forward is V's row 0 and its LSE is scale * q0.k0, every
-// output is finite, and bad arguments come back as the documented status codes.
+// checks what needs no reference implementation: the two forwards agree (to 1e-2
+// in O and 1e-4 in LSE: on this small causal grid fa_fwd takes the key-split
+// kernel, which adds the two key halves' sums in another order), row 0 of a
+// causal forward is V's row 0 and its LSE is scale * q0.k0, every output is
+// finite, and bad arguments come back as the documented status codes.
 // Prints "c_example ok" and returns 0 on success.
 #include <hip/hip_runtime.h>
 
@@ -88,8 +90,11 @@ int main() {
     hipMemcpy(hdq.data(), dq, n * 2, hipMemcpyDeviceToHost);
     hipMemcpy(hdk.data(), dk, n * 2, hipMemcpyDeviceToHost);
     hipMemcpy(hdv.data(), dv, n * 2, hipMemcpyDeviceToHost);
-    CHECK(ho == ho2 && std::memcmp(hl.data(), hl2.data(), hl.size() * 4) == 0,
-          "persistent forward differs from fa_fwd");
+    for (size_t i = 0; i < n; ++i)
+        CHECK(std::fabs(from_bf16(ho[i]) - from_bf16(ho2[i])) <= 1e-2f,
+              "persistent forward's O differs from fa_fwd's");
+    for (size_t i = 0; i < hl.size(); ++i)
+        CHECK(std::fabs(hl[i] - hl2[i]) <= 1e-4f, "persistent forward's LSE differs from fa_fwd's");
     for (size_t i = 0; i < n; ++i)
         CHECK(std::isfinite(from_bf16(ho[i])) && std::isfinite(from_bf16(hdq[i])) &&
                   std::isfinite(from_bf16(hdk[i])) && std::isfinite(from_bf16(hdv[i])),

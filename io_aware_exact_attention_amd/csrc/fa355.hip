@@ -124,16 +124,75 @@ int launch_bwd_dq_d(AttnParams p, int causal, hipStream_t s) {
                   : launch(fa_bwd_dq_kernel<D, false, VARLEN, DOT>, grid, Q::NW * 64, s, p);
 }
 
+// Work-group slots of the current device: 2 forward work-groups per CU.
+int fwd_slots(int* slots) {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        return FA_ERR_LAUNCH;
+    *slots = 2 * cus;
+    return FA_OK;
+}
+
+template <int D>
+int launch_bwd_fused_d(AttnParams p, int causal, hipStream_t s) {
+    using KV = BwdKVCfg<D>;
+    using Q = BwdQCfg<D>;
+    p.n_tiles = (p.nk + KV::BN - 1) / KV::BN;
+    const int64_t grid = ((int64_t)p.n_tiles + (p.nq + Q::BM - 1) / Q::BM) * p.H * p.batch;
+    if (grid > INT_MAX) return FA_ERR_SHAPE;
+    return causal ? launch(fa_bwd_fused_kernel<D, true>, (int)grid, KV::NW * 64, s, p)
+                  : launch(fa_bwd_fused_kernel<D, false>, (int)grid, KV::NW * 64, s, p);
+}
+
+// Dense backwards whose dK/dV and dQ work items (128-row tiles) together number
+// at most this many per CU run both passes in one launch (fa_bwd_fused_kernel,
+// after the row-dot kernel).  Measured on MI355X (fa_bwd, both forms bitwise
+// equal): causal, 12-27% faster from 1 to 4 items per CU and 10-15% at 8, equal
+// at 16, and 11-15% slower at 32 or more, where the longest-first order over all
+// heads loses the per-head L2 sharing of the two separate kernels; non-causal
+// (every tile equally long), 8% faster at 2 items per CU but 12% slower at 4,
+// where the separate kernels' single rounds are already balanced and the
+// separate row-dot kernel costs more than the merged tails save.
+#ifndef FA355_FUSED_BWD_CAUSAL_ITEMS_PER_CU
+#define FA355_FUSED_BWD_CAUSAL_ITEMS_PER_CU 8
+#endif
+#ifndef FA355_FUSED_BWD_FULL_ITEMS_PER_CU
+#define FA355_FUSED_BWD_FULL_ITEMS_PER_CU 2
+#endif
+
+int use_fused_bwd(const AttnParams& p, int causal, bool* fused) {
+    int slots = 0;
+    const int st = fwd_slots(&slots);   // two work-groups per CU
+    if (st) return st;
+    const int64_t items = ((int64_t)(p.nk + 127) / 128 + (p.nq + 127) / 128) * p.H * p.batch;
+    const int64_t per_cu = causal ? FA355_FUSED_BWD_CAUSAL_ITEMS_PER_CU : FA355_FUSED_BWD_FULL_ITEMS_PER_CU;
+    *fused = items <= per_cu * (slots / 2);
+    return FA_OK;
+}
+
 // The whole backward is kStageDqDot (the dQ kernel with the row-dot folded in:
-// it writes -D and LSE * log2(e) as well as dQ), then dK/dV.  The row-dot kernel
-// alone (kStageDot) fills the same workspace for the stand-alone dK/dV and dQ
-// stages.  Stages run in this order: dQ + row-dot, row-dot, dK/dV, dQ.
+// it writes -D and LSE * log2(e) as well as dQ), then dK/dV; for small dense
+// grids it is the row-dot kernel, then both passes in one launch.  The row-dot
+// kernel alone (kStageDot) fills the same workspace for the stand-alone dK/dV
+// and dQ stages.  Stages run in this order: dQ + row-dot, row-dot, dK/dV, dQ.
 enum BwdStage { kStageDot = 1, kStageDkdv = 2, kStageDq = 4, kStageDqDot = 8,
                 kStageAll = kStageDqDot | kStageDkdv };
 
 template <bool VARLEN>
 int launch_bwd(const AttnParams& p, int d, int causal, hipStream_t s, int stages = kStageAll) {
     int st = FA_OK;
+    if (!VARLEN && stages == kStageAll) {
+        bool fused = false;
+        st = use_fused_bwd(p, causal, &fused);
+        if (st) return st;
+        if (fused) {
+            st = d == 64 ? launch_bwd_dot_d<64, VARLEN>(p, s) : launch_bwd_dot_d<128, VARLEN>(p, s);
+            if (!st)
+                st = d == 64 ? launch_bwd_fused_d<64>(p, causal, s) : launch_bwd_fused_d<128>(p, causal, s);
+            return st;
+        }
+    }
     if (stages & kStageDqDot)
         st = d == 64 ? launch_bwd_dq_d<64, VARLEN, true>(p, causal, s)
                      : launch_bwd_dq_d<128, VARLEN, true>(p, causal, s);
@@ -274,15 +333,6 @@ int prepare_fwd(const void* q, const void* k, const void* v, void* o, float* lse
     return FA_OK;
 }
 
-// Work-group slots of the current device: 2 forward work-groups per CU.
-int fwd_slots(int* slots) {
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-        return FA_ERR_LAUNCH;
-    *slots = 2 * cus;
-    return FA_OK;
-}
 
 // The persistent forward on a grid of about as many work-groups as the CUs hold
 // at once (a multiple of the 8 XCDs).

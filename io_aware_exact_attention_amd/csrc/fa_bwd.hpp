@@ -124,11 +124,12 @@ __global__ __launch_bounds__(256) void fa_bwd_dot_kernel(AttnParams p) {
 // dP = dO V^T row-wise.  Query rows stream in stages of 32 (Q, dO, LSE, D),
 // double-buffered.  Two work-groups share a CU (256 registers per lane), so one
 // work-group's exp / dS arithmetic overlaps the other's matrix products.
+//
+// One work item: key tile `tile` of (batch or sequence, head) pair `bh`, with
+// the work-group's LDS (BwdKVCfg<D>::LDS_BYTES) at `smem`.
 template <int D, bool CAUSAL, bool VARLEN>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void fa_bwd_dkdv_kernel(AttnParams p) {
+__device__ __forceinline__ void dkdv_item(const AttnParams& p, char* smem, int bh, int tile) {
     using C = BwdKVCfg<D>;
-    __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: scalar branches
@@ -137,8 +138,6 @@ void fa_bwd_dkdv_kernel(AttnParams p) {
     const int sl = lane & 15;
     const int g = (lane >> 4) & 1;
 
-    int bh, tile;   // low key tiles see the most query rows: first
-    xcd_work_item(blockIdx.x, p.n_tiles, p.H * p.batch, bh, tile);
     const int h = bh % p.H;
     const int b = bh / p.H;
     int qs, nq, ks, nk;
@@ -305,16 +304,26 @@ void fa_bwd_dkdv_kernel(AttnParams p) {
     }
 }
 
+template <int D, bool CAUSAL, bool VARLEN>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void fa_bwd_dkdv_kernel(AttnParams p) {
+    __shared__ __attribute__((aligned(1024))) char smem[BwdKVCfg<D>::LDS_BYTES];
+    int bh, tile;   // low key tiles see the most query rows: first
+    xcd_work_item(blockIdx.x, p.n_tiles, p.H * p.batch, bh, tile);
+    dkdv_item<D, CAUSAL, VARLEN>(p, smem, bh, tile);
+}
+
 // ---------------------------------------------------------------------------
 // 3. dQ (query-tile outer).  With DOT it first computes D_i = rowsum(dO * O) of
 // its own rows (kernel 1's products, summed in kernel 1's pairwise order, so the
 // values are bitwise the same) and stores -D_i and LSE_i * log2(e) for the dK/dV
 // kernel, which must then run after it.
+//
+// One work item: query tile `tile` of (batch or sequence, head) pair `bh`, with
+// the work-group's LDS (BwdQCfg<D>::LDS_BYTES) at `smem`.
 template <int D, bool CAUSAL, bool VARLEN, bool DOT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void fa_bwd_dq_kernel(AttnParams p) {
+__device__ __forceinline__ void dq_item(const AttnParams& p, char* smem, int bh, int tile) {
     using C = BwdQCfg<D>;
-    __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -323,9 +332,6 @@ void fa_bwd_dq_kernel(AttnParams p) {
     const int sl = lane & 15;
     const int g = (lane >> 4) & 1;
 
-    int bh, rank;
-    xcd_work_item(blockIdx.x, p.n_tiles, p.H * p.batch, bh, rank);
-    const int tile = p.n_tiles - 1 - rank;
     const int h = bh % p.H;
     const int b = bh / p.H;
     int qs, nq, ks, nk;
@@ -523,6 +529,47 @@ void fa_bwd_dq_kernel(AttnParams p) {
                 store8(optr + d0, acc[cb][4 * rg] * sc, acc[cb][4 * rg + 1] * sc,
                        acc[cb][4 * rg + 2] * sc, acc[cb][4 * rg + 3] * sc);
             }
+    }
+}
+
+template <int D, bool CAUSAL, bool VARLEN, bool DOT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void fa_bwd_dq_kernel(AttnParams p) {
+    __shared__ __attribute__((aligned(1024))) char smem[BwdQCfg<D>::LDS_BYTES];
+    int bh, rank;   // longest causal rows first
+    xcd_work_item(blockIdx.x, p.n_tiles, p.H * p.batch, bh, rank);
+    dq_item<D, CAUSAL, VARLEN, DOT>(p, smem, bh, p.n_tiles - 1 - rank);
+}
+
+// ---------------------------------------------------------------------------
+// 4. dK/dV and dQ in one launch, for grids too small to fill the GPU twice over.
+// The two passes are independent once -D and LSE * log2(e) are in the workspace
+// (kernel 1 runs before this one), so one grid holds both passes' work items,
+// interleaved (even ids dK/dV, odd ids dQ; the surplus of the larger pass last),
+// each pass longest first over all (batch, head) pairs (lpt_work_item).  A short
+// grid then keeps its CUs busy with the other pass's items instead of draining
+// two causal tails one after the other.  p.n_tiles is the dK/dV pass's key-tile
+// count.
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void fa_bwd_fused_kernel(AttnParams p) {
+    constexpr int LDS = BwdKVCfg<D>::LDS_BYTES > BwdQCfg<D>::LDS_BYTES ? BwdKVCfg<D>::LDS_BYTES
+                                                                        : BwdQCfg<D>::LDS_BYTES;
+    __shared__ __attribute__((aligned(1024))) char smem[LDS];
+    const int pairs = p.H * p.batch;
+    const int n_kv_tiles = p.n_tiles;
+    const int n_q_tiles = (p.nq + BwdQCfg<D>::BM - 1) / BwdQCfg<D>::BM;
+    const int n1 = n_kv_tiles * pairs;
+    const int n2 = n_q_tiles * pairs;
+    const int m = min(n1, n2);
+    const int id = blockIdx.x;
+    int bh, rank;
+    if (id < 2 * m ? !(id & 1) : n1 > n2) {
+        lpt_work_item(id < 2 * m ? id >> 1 : id - m, n_kv_tiles, pairs, bh, rank);
+        dkdv_item<D, CAUSAL, false>(p, smem, bh, rank);
+    } else {
+        lpt_work_item(id < 2 * m ? id >> 1 : id - m, n_q_tiles, pairs, bh, rank);
+        dq_item<D, CAUSAL, false, false>(p, smem, bh, n_q_tiles - 1 - rank);
     }
 }
 
