@@ -20,7 +20,7 @@
 // gfx950 mapping (one work-group = 4 waves = BM 128 query rows, 32 per wave):
 //   * Q rows stay in registers for the whole kernel as the B operand of
 //     S^T = K Q^T (v_mfma_f32_32x32x16_bf16, fp32 accumulation).
-//   * K and V tiles (BN = 64 rows) stream from HBM into LDS with direct
+//   * K and V tiles (BN = 64 rows at d = 128, 128 at d = 64) stream from HBM into LDS with direct
 //     global->LDS 16-byte loads, double-buffered so the next tile's load
 //     overlaps this tile's math; one barrier per tile.
 //   * Because S^T's accumulator gives each lane one query and 16 keys per
@@ -39,11 +39,16 @@
 
 namespace fa355 {
 
-template <int D>
+// Key tiles of 64 rows at d = 128 and 128 rows at d = 64: a tile's barrier, row
+// maximum exchange and rescale test then cover as many bytes of K and V either
+// way (measured at d = 64 against 64-row tiles: B4 H16 N1024 non-causal 6%
+// faster, B8 H16 N4096 2-2.5%, B4 H16 N1024 causal the same).  The key-split
+// kernel keeps 64-row tiles at d = 64 (at 128 it needs 8 bytes of scratch).
+template <int D, int BN_ = (D == 64 ? 128 : 64)>
 struct FwdCfg {
     static constexpr int NW = 4;                 // waves per work-group
     static constexpr int BM = 32 * NW;           // query rows per work-group
-    static constexpr int BN = 64;                // key rows per tile
+    static constexpr int BN = BN_;               // key rows per tile
     static constexpr int ROW_BYTES = D * 2;
     static constexpr int CPR = D / 8;            // 16-byte chunks per row
     static constexpr int TILE_BYTES = BN * ROW_BYTES;
@@ -73,7 +78,7 @@ struct FwdCfg {
 // tile would (scale each by e^(m_half - m_max), add) and writes the output.
 template <int D, bool CAUSAL, bool VARLEN, int SPLIT = 1>
 __device__ __forceinline__ void fwd_tile(const AttnParams& p, char* smem, int bh, int tile) {
-    using C = FwdCfg<D>;
+    using C = FwdCfg<D, SPLIT == 2 ? 64 : FwdCfg<D>::BN>;
     static_assert(SPLIT == 1 || SPLIT == 2, "one or two key halves");
     const int lane = threadIdx.x & 63;
     const int wave = (threadIdx.x >> 6) & (C::NW - 1);   // row block of this wave
@@ -372,7 +377,7 @@ void fa_fwd_kernel(AttnParams p) {
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fa_fwd_split_kernel(AttnParams p) {
-    __shared__ __attribute__((aligned(1024))) char smem[2 * FwdCfg<D>::LDS_BYTES];
+    __shared__ __attribute__((aligned(1024))) char smem[2 * FwdCfg<D, 64>::LDS_BYTES];
     int bh, rank;
     lpt_work_item(blockIdx.x, p.n_tiles, p.H * p.batch, bh, rank);
     fwd_tile<D, CAUSAL, false, 2>(p, smem, bh, p.n_tiles - 1 - rank);
