@@ -237,11 +237,15 @@ __device__ __forceinline__ void dkdv_item(const AttnParams& p, char* smem, int b
         }
 
         // masked scores become -inf so that their P is exactly 0
+        // (row q0 + 4 h2 + off of register r, off = 8 (r / 4) + r % 4, is masked iff
+        // off < key - q0 - 4 h2 (causal) or off >= nq - q0 - 4 h2)
         if ((CAUSAL && q0 < kw0 + 31) || (q0 + 31 >= nq)) {
+            const int lo = CAUSAL ? key - q0 - 4 * h2 : -1;
+            const int hi = nq - q0 - 4 * h2;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int qrow = q0 + 8 * (r >> 2) + 4 * h2 + (r & 3);
-                if ((CAUSAL && key > qrow) || qrow >= nq) s[r] = kNegInf;
+                const int off = 8 * (r >> 2) + (r & 3);
+                if (off < lo || off >= hi) s[r] = kNegInf;
             }
         }
         // P = exp(scale*S - LSE) = exp2(S * scale*log2(e) - LSE*log2(e)), dS = P * (dP - D)
@@ -445,12 +449,13 @@ __device__ __forceinline__ void dq_item(const AttnParams& p, char* smem, int bh,
                     dpT = mfma_32x32x16(lds_read16(vt + off), gf[k2], dpT);
                 }
                 // masked scores become -inf so that their P is exactly 0
+                // (key kv0 + 32 kb + 4 h2 + off, off = 8 (r / 4) + r % 4, is masked iff it
+                // exceeds min(qi, nk - 1) causal, nk - 1 otherwise)
                 if constexpr (decltype(masked)::value) {
+                    const int lim = (CAUSAL ? min(qi, nk - 1) : nk - 1) - kv0 - kb * 32 - 4 * h2;
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int kj = kv0 + kb * 32 + 8 * (r >> 2) + 4 * h2 + (r & 3);
-                        if ((CAUSAL && kj > qi) || kj >= nk) sT[r] = kNegInf;
-                    }
+                    for (int r = 0; r < 16; ++r)
+                        if (8 * (r >> 2) + (r & 3) > lim) sT[r] = kNegInf;
                 }
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {

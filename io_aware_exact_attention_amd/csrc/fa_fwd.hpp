@@ -175,15 +175,17 @@ __device__ __forceinline__ void fwd_tile(const AttnParams& p, char* smem, int bh
                 sc[kb] = mfma_32x32x16(lds_read16(kt + koff[st] + kb * 32 * C::ROW_BYTES), qf[st], sc[kb]);
     };
     // causal diagonal / ragged tail of key tile t
+    // (a key is masked iff it exceeds the last key the row may see, min(qi, nk - 1)
+    // causal, nk - 1 otherwise; relative to the lane's first key of the tile that is
+    // one compare of each register's constant key offset)
     auto mask = [&](f32x16 (&sc)[C::KB], int t) __attribute__((always_inline)) {
         const int kv0 = (kt0 + t) * C::BN;
+        const int lim = (CAUSAL ? min(qi, nk - 1) : nk - 1) - kv0 - 4 * h2;
 #pragma unroll
         for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int key = kv0 + kb * 32 + 8 * (r >> 2) + 4 * h2 + (r & 3);
-                if ((CAUSAL && key > qi) || key >= nk) sc[kb][r] = kNegInf;
-            }
+            for (int r = 0; r < 16; ++r)
+                if (kb * 32 + 8 * (r >> 2) + (r & 3) > lim) sc[kb][r] = kNegInf;
     };
     // new running maximum from the held scores: sets m, alpha, mc
     auto row_max = [&](const f32x16 (&sc)[C::KB]) __attribute__((always_inline)) {
