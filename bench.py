@@ -614,11 +614,15 @@ def main():
     achieved = kern_flops[dom] / (kern_ms[dom] * 1e-3) / 1e12
     roof = {"kernel": names[dom], "bound": "mfma", "achieved": round(achieved, 2),
             "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4)}
-    roof["traffic"] = traffic.get(names[dom]) if traffic else None
+    def traffic_of(name):   # "a + b": the kernels one entry point launches, summed
+        parts = [traffic.get(k) for k in name.split(" + ")] if traffic else [None]
+        return sum(parts) if all(t is not None for t in parts) else None
+
+    roof["traffic"] = traffic_of(names[dom])
     roof["algorithmic_bytes"] = kern_bytes[dom]
     for n, b_alg in zip(names, kern_bytes):
         kern[n]["algorithmic_bytes"] = b_alg
-        kern[n]["traffic"] = traffic.get(n) if traffic else None
+        kern[n]["traffic"] = traffic_of(n)
 
     t_fwd = kern_ms[0]
     t_bwd = sum(kern_ms[1:])
