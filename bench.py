@@ -606,9 +606,10 @@ def main():
     tok = B * N * H
     kern_bytes = [cnt["bytes_fwd"], tok * (5 * 2 * d + 4) + tok * (2 * d + 8),
                   tok * (4 * 2 * d + 8) + tok * 2 * 2 * d]
-    if fused:   # the row-dot kernel (o, dout, LSE in; -D, LSE*log2(e) out), then both passes
-        # and both passes together (q, k, v, dout, -D, LSE*log2(e) in; dq, dk, dv out)
-        kern_bytes = [kern_bytes[0], tok * (2 * 2 * d + 4 + 8) + tok * (4 * 2 * d + 8) + tok * 3 * 2 * d]
+    if fused:   # the row-dot kernel (o, dout, LSE in; -D, LSE*log2(e) out), then the two
+        # passes, each reading q, k, v, dout, -D and LSE*log2(e) once (dq; dk, dv out)
+        kern_bytes = [kern_bytes[0], tok * (2 * 2 * d + 4 + 8) + tok * (4 * 2 * d + 8 + 2 * d)
+                      + tok * (4 * 2 * d + 8 + 2 * 2 * d)]
     traffic = measured_traffic(w.name)
     dom = max(range(len(names)), key=lambda i: kern_ms[i])
     achieved = kern_flops[dom] / (kern_ms[dom] * 1e-3) / 1e12
