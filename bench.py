@@ -30,6 +30,8 @@ from io_aware_exact_attention_amd import workloads as wl
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+TARGET_FWD_PCT = 50.0       # causal bf16 forward, % of the dense bf16 MFMA peak
+TARGET_FWD_BWD_PCT = 35.0   # forward + backward
 
 CALIB_BYTES = 256 << 20     # size of the counter-calibration copy
 
@@ -653,6 +655,10 @@ def main():
         "fwd_bwd_tflops_kernels": round(fb_tf_events, 2),
         "fwd_bwd_pct_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "fwd_hbm_gbs": round(cnt["bytes_fwd"] / (t_fwd * 1e-3) / 1e9, 1),
+        # the performance targets set for this path on its headline workload
+        "targets": {"fwd_pct_peak": TARGET_FWD_PCT, "fwd_bwd_pct_peak": TARGET_FWD_BWD_PCT,
+                    "fwd_met": 100 * fwd_tf / PEAK_BF16_TFLOPS >= TARGET_FWD_PCT,
+                    "fwd_bwd_met": 100 * value / PEAK_BF16_TFLOPS >= TARGET_FWD_BWD_PCT},
         "kernels": kern,
         "roofline": roof,
         "device": torch.cuda.get_device_name(0),
