@@ -346,14 +346,11 @@ int launch_fwd_persistent(const AttnParams& p, int d, int causal, int slots, hip
                   : launch(fa_fwd_persistent_kernel<128, false>, grid, FwdCfg<128>::NW * 64, s, p);
 }
 
-// The key-split forward: one 8-wave work-group per query tile.
-int launch_fwd_split(const AttnParams& p, int d, int causal, hipStream_t s) {
+// The key-split forward (causal grids only): one 8-wave work-group per query tile.
+int launch_fwd_split(const AttnParams& p, int d, hipStream_t s) {
     const int grid = p.n_tiles * p.H * p.batch;
-    if (d == 64)
-        return causal ? launch(fa_fwd_split_kernel<64, true>, grid, 2 * FwdCfg<64>::NW * 64, s, p)
-                      : launch(fa_fwd_split_kernel<64, false>, grid, 2 * FwdCfg<64>::NW * 64, s, p);
-    return causal ? launch(fa_fwd_split_kernel<128, true>, grid, 2 * FwdCfg<128>::NW * 64, s, p)
-                  : launch(fa_fwd_split_kernel<128, false>, grid, 2 * FwdCfg<128>::NW * 64, s, p);
+    return d == 64 ? launch(fa_fwd_split_kernel<64, true>, grid, 2 * FwdCfg<64>::NW * 64, s, p)
+                   : launch(fa_fwd_split_kernel<128, true>, grid, 2 * FwdCfg<128>::NW * 64, s, p);
 }
 
 }  // namespace
@@ -397,7 +394,7 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
     if (st) return st;
     const int64_t items = (int64_t)p.n_tiles * H * B;
     if (causal && (items <= slots / 2 || (items <= slots && p.n_tiles >= 16)))
-        return launch_fwd_split(p, d, causal, s);
+        return launch_fwd_split(p, d, s);
     if (items <= slots) return launch_fwd_persistent(p, d, causal, slots, s);
     return launch_fwd<false>(p, d, causal, s);
 }
