@@ -295,20 +295,13 @@ __device__ __forceinline__ void dkdv_item(const AttnParams& p, char* smem, int b
         if (it + 1 < n_q) step(it + 1, std::integral_constant<int, 1>{});
     }
 
-    if (key < nk) {
-        const int64_t off = (int64_t)(ks + key) * tok + h * D;
-        const float sc = p.scale;
-#pragma unroll
-        for (int cb = 0; cb < C::DBLK; ++cb)
-#pragma unroll
-            for (int rg = 0; rg < 4; ++rg) {
-                const int d0 = cb * 32 + 8 * rg + 4 * h2;
-                store8(p.dk + off + d0, dka[cb][4 * rg] * sc, dka[cb][4 * rg + 1] * sc,
-                       dka[cb][4 * rg + 2] * sc, dka[cb][4 * rg + 3] * sc);
-                store8(p.dv + off + d0, dva[cb][4 * rg], dva[cb][4 * rg + 1], dva[cb][4 * rg + 2],
-                       dva[cb][4 * rg + 3]);
-            }
-    }
+    // dV, then dK (times the scale), through this wave's LDS slice as whole
+    // 16-byte chunks of 4 rows per instruction
+    static_assert(C::NW * kRowSliceBytes<D> <= C::LDS_BYTES, "row slices fit the LDS");
+    __syncthreads();   // every wave is done with the V tile and the stage buffers
+    FA_LDS char* slice = lds + wave * kRowSliceBytes<D>;
+    store_rows_via_lds<D>(slice, dva, 1.f, p.dv + (int64_t)ks * tok + h * D, tok, kw0, nk, lane);
+    store_rows_via_lds<D>(slice, dka, p.scale, p.dk + (int64_t)ks * tok + h * D, tok, kw0, nk, lane);
 }
 
 template <int D, bool CAUSAL, bool VARLEN>
@@ -526,18 +519,11 @@ __device__ __forceinline__ void dq_item(const AttnParams& p, char* smem, int bh,
         if (t + 1 < n_kv) step(t + 1, std::integral_constant<int, 1>{});
     }
 
-    if (qi < nq) {
-        bf16* optr = p.dq + (int64_t)(qs + qi) * tok + h * D;
-        const float sc = p.scale;
-#pragma unroll
-        for (int cb = 0; cb < C::DBLK; ++cb)
-#pragma unroll
-            for (int rg = 0; rg < 4; ++rg) {
-                const int d0 = cb * 32 + 8 * rg + 4 * h2;
-                store8(optr + d0, acc[cb][4 * rg] * sc, acc[cb][4 * rg + 1] * sc,
-                       acc[cb][4 * rg + 2] * sc, acc[cb][4 * rg + 3] * sc);
-            }
-    }
+    // dQ (times the scale) through this wave's LDS slice as whole 16-byte chunks
+    static_assert(C::NW * kRowSliceBytes<D> <= C::LDS_BYTES, "row slices fit the K/V buffers");
+    __syncthreads();   // every wave is done with the K/V buffers
+    store_rows_via_lds<D>(lds + wave * kRowSliceBytes<D>, acc, p.scale, p.dq + (int64_t)qs * tok + h * D,
+                          tok, qw0, nq, lane);
 }
 
 template <int D, bool CAUSAL, bool VARLEN, bool DOT>

