@@ -49,7 +49,10 @@ template <int D>
 struct BwdKVCfg {
     static constexpr int NW = 4;
     static constexpr int BN = 32 * NW;            // keys per work-group (32 per wave)
-    static constexpr int BMQ = 32;                // query rows per streamed stage
+    // query rows per streamed stage: two 32-row blocks at d = 64, so that a stage's
+    // barrier and loads carry as many products as one 32-row block at d = 128
+    static constexpr int BMQ = D == 64 ? 64 : 32;
+    static constexpr int RB = BMQ / 32;           // 32-row blocks per stage
     static constexpr int ROW_BYTES = D * 2;
     static constexpr int TILE_BYTES = BMQ * ROW_BYTES;
     static constexpr int V_BYTES = BN * ROW_BYTES;
@@ -205,89 +208,105 @@ __device__ __forceinline__ void dkdv_item(const AttnParams& p, char* smem, int b
     // as in the forward)
     auto step = [&](int it, auto buf) __attribute__((always_inline)) {
         constexpr int SB = decltype(buf)::value;   // this stage's buffer
-        const FA_LDS char* qt = lds + C::STAGE0 + SB * 2 * C::TILE_BYTES;
-        const FA_LDS char* gt = qt + C::TILE_BYTES;
-        const FA_LDS float* lse_t = (const FA_LDS float*)(lds + C::STATS0 + SB * C::STAT_BYTES);
-        const FA_LDS float* nd_t = lse_t + 64;
+        const FA_LDS char* qt_s = lds + C::STAGE0 + SB * 2 * C::TILE_BYTES;
+        const FA_LDS char* gt_s = qt_s + C::TILE_BYTES;
+        const FA_LDS float* lse_s = (const FA_LDS float*)(lds + C::STATS0 + SB * C::STAT_BYTES);
+        const FA_LDS float* nd_s = lse_s + 64;
         wait_vmem();
         __syncthreads();
         if (it + 1 < n_q) issue(it + 1);
-        const int q0 = stage_q0(it);
-        if (CAUSAL && q0 + 31 < kw0) return;   // every query here precedes every key
+        // one 32-row block of the stage: rows q0 .. q0 + 31, at row `row0` of the
+        // stage's tiles and statistics
+        auto block = [&](const int q0, const int row0) __attribute__((always_inline)) {
+            const FA_LDS char* qt = qt_s + row0 * C::ROW_BYTES;   // 32 more rows keep the swizzle
+            const FA_LDS char* gt = gt_s + row0 * C::ROW_BYTES;
+            const FA_LDS float* lse_t = lse_s + row0;
+            const FA_LDS float* nd_t = nd_s + row0;
 
-        // S = Q K^T and dP - D = dO V^T - D: rows are queries (this lane's rows are
-        // q0 + 8*(r/4) + 4*h2 + r%4), columns this wave's keys.  The dP
-        // accumulator starts at -D of its row.
-        f32x16 s, dp;
+            // S = Q K^T and dP - D = dO V^T - D: rows are queries (this lane's rows are
+            // q0 + 8*(r/4) + 4*h2 + r%4), columns this wave's keys.  The dP
+            // accumulator starts at -D of its row.
+            f32x16 s, dp;
 #pragma unroll
-        for (int rg = 0; rg < 4; ++rg) {
-            const f32x4 n4 = *reinterpret_cast<const FA_LDS f32x4*>(nd_t + 8 * rg + 4 * h2);
+            for (int rg = 0; rg < 4; ++rg) {
+                const f32x4 n4 = *reinterpret_cast<const FA_LDS f32x4*>(nd_t + 8 * rg + 4 * h2);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                s[4 * rg + e] = 0.f;
-                dp[4 * rg + e] = n4[e];
+                for (int e = 0; e < 4; ++e) {
+                    s[4 * rg + e] = 0.f;
+                    dp[4 * rg + e] = n4[e];
+                }
             }
-        }
 #pragma unroll
-        for (int k2 = 0; k2 < C::KSTEPS; ++k2) {
-            const int off = tile_off<D>(col, 2 * k2 + h2);
-            const bf16x8 vb = lds_read16(lds + tile_off<D>(wave * 32 + col, 2 * k2 + h2));
-            s = mfma_32x32x16(lds_read16(qt + off), kf[k2], s);
-            dp = mfma_32x32x16(lds_read16(gt + off), vb, dp);
-        }
+            for (int k2 = 0; k2 < C::KSTEPS; ++k2) {
+                const int off = tile_off<D>(col, 2 * k2 + h2);
+                const bf16x8 vb = lds_read16(lds + tile_off<D>(wave * 32 + col, 2 * k2 + h2));
+                s = mfma_32x32x16(lds_read16(qt + off), kf[k2], s);
+                dp = mfma_32x32x16(lds_read16(gt + off), vb, dp);
+            }
 
-        // masked scores become -inf so that their P is exactly 0
-        // (row q0 + 4 h2 + off of register r, off = 8 (r / 4) + r % 4, is masked iff
-        // off < key - q0 - 4 h2 (causal) or off >= nq - q0 - 4 h2)
-        if ((CAUSAL && q0 < kw0 + 31) || (q0 + 31 >= nq)) {
-            const int lo = CAUSAL ? key - q0 - 4 * h2 : -1;
-            const int hi = nq - q0 - 4 * h2;
+            // masked scores become -inf so that their P is exactly 0
+            // (row q0 + 4 h2 + off of register r, off = 8 (r / 4) + r % 4, is masked iff
+            // off < key - q0 - 4 h2 (causal) or off >= nq - q0 - 4 h2)
+            if ((CAUSAL && q0 < kw0 + 31) || (q0 + 31 >= nq)) {
+                const int lo = CAUSAL ? key - q0 - 4 * h2 : -1;
+                const int hi = nq - q0 - 4 * h2;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int off = 8 * (r >> 2) + (r & 3);
-                if (off < lo || off >= hi) s[r] = kNegInf;
+                for (int r = 0; r < 16; ++r) {
+                    const int off = 8 * (r >> 2) + (r & 3);
+                    if (off < lo || off >= hi) s[r] = kNegInf;
+                }
             }
-        }
-        // P = exp(scale*S - LSE) = exp2(S * scale*log2(e) - LSE*log2(e)), dS = P * (dP - D)
+            // P = exp(scale*S - LSE) = exp2(S * scale*log2(e) - LSE*log2(e)), dS = P * (dP - D)
 #pragma unroll
-        for (int rg = 0; rg < 4; ++rg) {
-            const f32x4 l4 = *reinterpret_cast<const FA_LDS f32x4*>(lse_t + 8 * rg + 4 * h2);
+            for (int rg = 0; rg < 4; ++rg) {
+                const f32x4 l4 = *reinterpret_cast<const FA_LDS f32x4*>(lse_t + 8 * rg + 4 * h2);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = 4 * rg + e;
-                const float pr = fast_exp2(__builtin_fmaf(s[r], c, -l4[e]));
-                s[r] = pr;
-                dp[r] = pr * dp[r];
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 4 * rg + e;
+                    const float pr = fast_exp2(__builtin_fmaf(s[r], c, -l4[e]));
+                    s[r] = pr;
+                    dp[r] = pr * dp[r];
+                }
             }
-        }
-        bf16x8 pb[2], db[2];
+            bf16x8 pb[2], db[2];
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            float tp[8], td[8];
+            for (int kk = 0; kk < 2; ++kk) {
+                float tp[8], td[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                tp[e] = s[8 * kk + e];
-                td[e] = dp[8 * kk + e];
+                for (int e = 0; e < 8; ++e) {
+                    tp[e] = s[8 * kk + e];
+                    td[e] = dp[8 * kk + e];
+                }
+                pb[kk] = pack8(tp);
+                db[kk] = pack8(td);
             }
-            pb[kk] = pack8(tp);
-            db[kk] = pack8(td);
-        }
 
-        // dV^T[dim][key] += dO^T P,  dK^T[dim][key] += Q^T dS
+            // dV^T[dim][key] += dO^T P,  dK^T[dim][key] += Q^T dS
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
+            for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
-            for (int cb = 0; cb < C::DBLK; ++cb) {
-                const int c0 = cb * 32 + 16 * g;
-                // rows 16*kk + 4*h2 (+8): 16 more rows keep the swizzle, so kk only
-                // adds an immediate offset
-                const int o1 = tr_off<D>(4 * h2, c0, sl) + kk * 16 * C::ROW_BYTES;
-                const int o2 = tr_off<D>(4 * h2 + 8, c0, sl) + kk * 16 * C::ROW_BYTES;
-                const bf16x8 ag = join(lds_read_tr(gt + o1), lds_read_tr(gt + o2));
-                dva[cb] = mfma_32x32x16(ag, pb[kk], dva[cb]);
-                const bf16x8 aq = join(lds_read_tr(qt + o1), lds_read_tr(qt + o2));
-                dka[cb] = mfma_32x32x16(aq, db[kk], dka[cb]);
+                for (int cb = 0; cb < C::DBLK; ++cb) {
+                    const int c0 = cb * 32 + 16 * g;
+                    // rows 16*kk + 4*h2 (+8): 16 more rows keep the swizzle, so kk only
+                    // adds an immediate offset
+                    const int o1 = tr_off<D>(4 * h2, c0, sl) + kk * 16 * C::ROW_BYTES;
+                    const int o2 = tr_off<D>(4 * h2 + 8, c0, sl) + kk * 16 * C::ROW_BYTES;
+                    const bf16x8 ag = join(lds_read_tr(gt + o1), lds_read_tr(gt + o2));
+                    dva[cb] = mfma_32x32x16(ag, pb[kk], dva[cb]);
+                    const bf16x8 aq = join(lds_read_tr(qt + o1), lds_read_tr(qt + o2));
+                    dka[cb] = mfma_32x32x16(aq, db[kk], dka[cb]);
+                }
             }
+        };
+        const int q0s = stage_q0(it);
+        // blocks from the last rows down, as the stages run: the products accumulate
+        // in the order of 32-row stages (bitwise the same dK, dV)
+#pragma unroll
+        for (int rb = C::RB - 1; rb >= 0; --rb) {
+            const int q0 = q0s + 32 * rb;
+            // every query of the block precedes every key of the wave, or lies past the rows
+            if ((CAUSAL && q0 + 31 < kw0) || q0 >= nq) continue;
+            block(q0, 32 * rb);
         }
     };
     for (int it = 0; it < n_q; it += 2) {   // two stages per trip: buffer offsets are constants
