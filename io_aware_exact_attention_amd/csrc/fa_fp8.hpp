@@ -284,7 +284,10 @@ template <bool CAUSAL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3)))
 void fa_fwd_fp8_kernel(Fp8AttnParams p) {
     using C = Fp8Cfg;
-    __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
+    // the K/V buffers, or at the end the 4 waves' row slices of the O epilogue
+    constexpr int LDS = C::LDS_BYTES > C::NW * kRowSliceBytes<kFp8D> ? C::LDS_BYTES
+                                                                      : C::NW * kRowSliceBytes<kFp8D>;
+    __shared__ __attribute__((aligned(1024))) char smem[LDS];
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -465,16 +468,11 @@ void fa_fwd_fp8_kernel(Fp8AttnParams p) {
 
     const float lt = sum_halves(l);
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    // O through this wave's LDS slice, out as whole 16-byte chunks (as the bf16 forward)
+    __syncthreads();   // every wave is done with the K/V buffers
+    store_rows_via_lds<kFp8D>((FA_LDS char*)smem + wave * kRowSliceBytes<kFp8D>, acc, inv,
+                              p.o + (int64_t)b * nq * tok + h * kFp8D, tok, qw0, nq, lane);
     if (qi < nq) {
-        bf16* optr = p.o + ((int64_t)b * nq + qi) * tok + h * kFp8D;
-#pragma unroll
-        for (int cb = 0; cb < 4; ++cb)
-#pragma unroll
-            for (int rg = 0; rg < 4; ++rg) {
-                const int d0 = cb * 32 + 8 * rg + 4 * h2;
-                store8(optr + d0, acc[cb][4 * rg] * inv, acc[cb][4 * rg + 1] * inv,
-                       acc[cb][4 * rg + 2] * inv, acc[cb][4 * rg + 3] * inv);
-            }
         if (h2 == 0) {
             p.lse[((int64_t)b * p.H + h) * nq + qi] =
                 lt > 0.f ? (m + __builtin_amdgcn_logf(lt) - (8.f - kFp8RescaleLog2)) * kLn2 : kNegInf;
