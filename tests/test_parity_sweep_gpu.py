@@ -56,6 +56,37 @@ def test_sweep_dense_fwd_bwd_persistent(case):
         assert torch.equal(o2.cpu(), g["o"].cpu()) and torch.equal(l2.cpu(), g["lse"].cpu())
 
 
+def _dense_cases_large(n=8, seed=5152):
+    """Shapes large enough that some take the one-tile-per-work-group forward and
+    the two-kernel backward (grids beyond a few work-groups per CU), with ragged
+    tails, alongside ones that take the key-split forward and one-launch backward."""
+    out = [
+        (3, 1900, 1900, 32, 128, True),    # one-tile forward, two-kernel backward (256 CUs)
+        (2, 1500, 1300, 16, 64, False),    # persistent forward, two-kernel backward
+        (2, 2100, 2100, 24, 64, True),     # one-tile forward, one-launch backward
+    ]
+    rng = random.Random(seed)
+    for _ in range(n):
+        causal = rng.random() < 0.6
+        nq = rng.choice([600, 1000, 1500, 2048, 2500])
+        nk = nq if causal else rng.choice([700, 1100, 2049])
+        out.append((rng.choice([1, 2]), nq, nk, rng.choice([4, 8, 12, 16]), rng.choice([64, 128]), causal))
+    return out
+
+
+@pytest.mark.parametrize("case", _dense_cases_large(), ids=_ids)
+def test_sweep_dense_large(case):
+    gu.need_gpu()
+    B, Nq, Nk, H, d, causal = case
+    gu.announce(f"sweep dense large {case}")
+    x = wl.make_dense(B, Nq, H, d, seed=9300 + Nq * 3 + Nk + H + d, Nk=Nk)
+    scale = d ** -0.5
+    g = gu.run_dense(x, scale, causal)
+    r = gu.oracle_dense(x, scale, causal)
+    gu.check_forward(g["o"], g["lse"], r["o"], r["lse"], str(case))
+    gu.check_grads(g["grads"], r["grads"], str(case))
+
+
 def _decode_cases(n=6, seed=5151):
     rng = random.Random(seed)
     out = []
