@@ -462,13 +462,14 @@ def fa_fwd_kernel_name(B: int, H: int, N: int, causal: bool) -> str:
     """The kernel fa_fwd launches for a dense shape (its documented choice): the
     key-split kernel for causal grids of at most one 128-row query tile per CU (or
     two per CU with at least 16 tiles per sequence), else the persistent kernel
-    when the tiles fit two per CU, else one work-group per tile."""
+    when the tiles fit two per CU or, causal, when a sequence has at most 32
+    tiles, else one work-group per tile."""
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     n_tiles = -(-N // 128)
     items = n_tiles * B * H
     if causal and (items <= cus or (items <= 2 * cus and n_tiles >= 16)):
         return "fa_fwd_split_kernel"
-    if items <= 2 * cus:
+    if items <= 2 * cus or (causal and n_tiles <= 32):
         return "fa_fwd_persistent_kernel"
     return "fa_fwd_kernel"
 

@@ -80,7 +80,8 @@ int fa_version(void);
  *     (max, sum, O) through LDS ("LLM Systems 22: Flash Attention", §4.1.5
  *     load balancing: the longest tile's chain of key tiles is halved);
  *   - otherwise, when the tiles fit on the GPU at once (two work-groups per
- *     CU): fa_fwd_persistent's kernel (bitwise the per-tile kernel's results);
+ *     CU), or causal with at most 32 query tiles per sequence (N <= 4096):
+ *     fa_fwd_persistent's kernel (bitwise the per-tile kernel's results);
  *   - otherwise one work-group per query tile.
  */
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -90,9 +91,11 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
  * Forward, dense batch, as a persistent kernel ("LLM Systems 22: Flash
  * Attention", §4.1.4 Persistent Kernels, §4.1.5 Load Balancing: longest-
  * processing-time first): a fixed grid of about as many work-groups as the CUs
- * hold at once loops over the query tiles, taken longest first (every pair's
- * tile with the most causal keys, then the next, ...), each XCD working on its
- * own (batch, head) pairs.  Arguments, results and errors as fa_fwd; the
+ * hold at once loops over the query tiles, each XCD working on its own (batch,
+ * head) pairs.  When the tiles fit in one round they are taken longest first
+ * over all pairs (every pair's tile with the most causal keys, then the next,
+ * ...); otherwise each XCD takes its pairs one after another, each pair's tiles
+ * longest first, so that its resident work-groups share a few pairs' K/V in L2.  Arguments, results and errors as fa_fwd; the
  * outputs are bitwise those of fa_fwd wherever fa_fwd does not take the
  * key-split kernel (the same tile computation).
  */

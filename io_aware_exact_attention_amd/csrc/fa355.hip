@@ -336,14 +336,23 @@ int prepare_fwd(const void* q, const void* k, const void* v, void* o, float* lse
 
 // The persistent forward on a grid of about as many work-groups as the CUs hold
 // at once (a multiple of the 8 XCDs).
+// Items are numbered longest first over all pairs when they fit in one round,
+// and pair by pair per XCD (the per-tile kernel's order) otherwise.
+template <int D, bool CAUSAL>
+int launch_fwd_persistent_d(const AttnParams& p, int grid, bool one_round, hipStream_t s) {
+    return one_round ? launch(fa_fwd_persistent_kernel<D, CAUSAL, false>, grid, FwdCfg<D>::NW * 64, s, p)
+                     : launch(fa_fwd_persistent_kernel<D, CAUSAL, true>, grid, FwdCfg<D>::NW * 64, s, p);
+}
+
 int launch_fwd_persistent(const AttnParams& p, int d, int causal, int slots, hipStream_t s) {
     const int64_t items = (int64_t)p.n_tiles * p.H * p.batch;
     const int grid = (int)std::max<int64_t>(8, std::min<int64_t>((int64_t)slots / 8 * 8, (items + 7) / 8 * 8));
+    const bool one_round = items <= grid;
     if (d == 64)
-        return causal ? launch(fa_fwd_persistent_kernel<64, true>, grid, FwdCfg<64>::NW * 64, s, p)
-                      : launch(fa_fwd_persistent_kernel<64, false>, grid, FwdCfg<64>::NW * 64, s, p);
-    return causal ? launch(fa_fwd_persistent_kernel<128, true>, grid, FwdCfg<128>::NW * 64, s, p)
-                  : launch(fa_fwd_persistent_kernel<128, false>, grid, FwdCfg<128>::NW * 64, s, p);
+        return causal ? launch_fwd_persistent_d<64, true>(p, grid, one_round, s)
+                      : launch_fwd_persistent_d<64, false>(p, grid, one_round, s);
+    return causal ? launch_fwd_persistent_d<128, true>(p, grid, one_round, s)
+                  : launch_fwd_persistent_d<128, false>(p, grid, one_round, s);
 }
 
 // The key-split forward (causal grids only): one 8-wave work-group per query tile.
@@ -387,15 +396,18 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
     // tiles on a CU: measured on MI355X, the key-split kernel was 17-28% faster
     // at 256 or 512 tiles of N = 4096 and 17% faster at 256 tiles of N = 1024,
     // but 8-10% slower at 512 tiles of N = 1024, where its second round of
-    // work-groups costs more than the halved chain saves.  Larger grids balance
-    // themselves as work-groups finish and run the per-tile kernel.
+    // work-groups costs more than the halved chain saves.  Larger causal grids of
+    // sequences up to 32 query tiles (N <= 4096) also run the persistent kernel,
+    // in the per-tile kernel's order (2.3% faster on B8 H16 N4096, 9-17% on
+    // B4 H16 N4096, B8 H16 N2048, B16 H16 N1024; equal at N = 8192, 1% slower at
+    // N = 32768, 2-8% slower non-causal); the rest run one work-group per tile.
     int slots = 0;
     st = fwd_slots(&slots);
     if (st) return st;
     const int64_t items = (int64_t)p.n_tiles * H * B;
     if (causal && (items <= slots / 2 || (items <= slots && p.n_tiles >= 16)))
         return launch_fwd_split(p, d, s);
-    if (items <= slots) return launch_fwd_persistent(p, d, causal, slots, s);
+    if (items <= slots || (causal && p.n_tiles <= 32)) return launch_fwd_persistent(p, d, causal, slots, s);
     return launch_fwd<false>(p, d, causal, s);
 }
 

@@ -397,18 +397,26 @@ void fa_fwd_split_kernel(AttnParams p) {
 
 // Persistent form ("LLM Systems 22: Flash Attention", §4.1.4 persistent kernels,
 // §4.1.5 longest-processing-time-first): a fixed grid (a multiple of 8, about
-// the number of work-groups the CUs hold at once) loops over the work items.
-// Items are numbered longest first -- all pairs' last query tile (the one with
-// the most causal keys), then all second-to-last ones, ... -- with item i on
-// XCD i % 8 taking pairs bh = i % 8 (mod 8), so each XCD's L2 sees only its
-// own heads.  The sorted list is dealt in rounds of one item per work-group,
-// alternating direction ("snake"): in even rounds work-group g takes item
-// round * grid + g, in odd rounds the work-groups of each XCD take theirs in
-// reverse order.  A plain round-robin deal gives work-group 0 the longest item
-// of every round (9% above the mean on B8 H16 N4096, 12% on N32768, which is
-// the kernel's tail); the snake deal keeps every work-group within one item
-// unit of the greedy longest-first schedule.  No atomics, no workspace.
-template <int D, bool CAUSAL>
+// the number of work-groups the CUs hold at once) loops over the work items,
+// dealt in rounds of one item per work-group, alternating direction ("snake"):
+// in even rounds work-group g takes item round * grid + g, in odd rounds the
+// work-groups of each XCD take theirs in reverse order.  A plain round-robin
+// deal gives work-group 0 the longest item of every round (9% above the mean on
+// B8 H16 N4096, 12% on N32768, which is the kernel's tail); the snake deal keeps
+// every work-group within one item unit of the greedy longest-first schedule.
+// Item i runs on XCD i % 8, and the items are numbered in one of two orders:
+//   * XCD_ORDER = false (lpt_work_item), longest first over all pairs: all
+//     pairs' last query tile (the one with the most causal keys), then all
+//     second-to-last ones, ...  For grids of one round, where it pairs long and
+//     short tiles on a CU.
+//   * XCD_ORDER = true (xcd_work_item, the per-tile kernel's order): each XCD
+//     takes its pairs one after another, each pair's tiles longest first, so the
+//     work-groups resident on an XCD work on about two pairs at a time and share
+//     their K/V in its L2 (longest first over all pairs keeps 16 pairs in flight
+//     per XCD on B8 H16 N4096, whose 2 MB of K/V each do not fit the 4 MB L2:
+//     0.636 against 0.611 ms).  For causal grids of several rounds.
+// No atomics, no workspace.
+template <int D, bool CAUSAL, bool XCD_ORDER>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fa_fwd_persistent_kernel(AttnParams p) {
     __shared__ __attribute__((aligned(1024))) char smem[FwdCfg<D>::LDS_BYTES];
@@ -421,7 +429,10 @@ void fa_fwd_persistent_kernel(AttnParams p) {
         const int it = base + ((r & 1) ? g_rev : g);
         if (it >= total) continue;
         int bh, rank;
-        lpt_work_item(it, p.n_tiles, bh_count, bh, rank);
+        if constexpr (XCD_ORDER)
+            xcd_work_item(it, p.n_tiles, bh_count, bh, rank);
+        else
+            lpt_work_item(it, p.n_tiles, bh_count, bh, rank);
         fwd_tile<D, CAUSAL, false>(p, smem, bh, p.n_tiles - 1 - rank);
         __syncthreads();   // the next item's loads reuse the LDS buffers
     }

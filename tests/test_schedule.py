@@ -47,11 +47,12 @@ def test_lpt_within_grahams_bound(seed):
     assert sum(sch.list_schedule(costs, m)[0]) == sum(costs)
 
 
-def _kernel_items(n_tiles, bh_count, grid):
+def _kernel_items(n_tiles, bh_count, grid, xcd_order=False):
     """The persistent forward kernel's assignment, restated: the items, numbered
-    longest first (item i -> (pair, rank), pairs dealt over the 8 XCDs), are
-    dealt in rounds of one per work-group, even rounds in work-group order, odd
-    rounds with each XCD's work-groups reversed (work-group g = 8 j + x takes
+    longest first over all pairs (item i -> (pair, rank), pairs dealt over the 8
+    XCDs) or, with xcd_order, pair by pair per XCD (the per-tile kernel's order),
+    are dealt in rounds of one per work-group, even rounds in work-group order,
+    odd rounds with each XCD's work-groups reversed (work-group g = 8 j + x takes
     item round * grid + 8 (grid/8 - 1 - j) + x); tile = n_tiles - 1 - rank."""
     out = {g: [] for g in range(grid)}
     total = n_tiles * bh_count
@@ -61,7 +62,14 @@ def _kernel_items(n_tiles, bh_count, grid):
             it = r * grid + (8 * (grid // 8 - 1 - g // 8) + g % 8 if r % 2 else g)
             if it >= total:
                 continue
-            if bh_count % 8 == 0:
+            if xcd_order:
+                if bh_count % 8 == 0:
+                    j = it // 8
+                    bh, rank = (j // n_tiles) * 8 + it % 8, j % n_tiles
+                else:
+                    L = (it % 8) * (total // 8) + it // 8 if total % 8 == 0 else it
+                    bh, rank = L // n_tiles, L % n_tiles
+            elif bh_count % 8 == 0:
                 per = bh_count // 8
                 j = it // 8
                 bh, rank = (j % per) * 8 + it % 8, j // per
@@ -94,6 +102,33 @@ def test_persistent_assignment(n_tiles, bh_count, grid):
     # the snake deal is within one cost unit of greedy LPT on these causal lists
     # (a round-robin deal is 9-12% above it on 32 x 128 and 256 x 16)
     assert static <= lpt + 1
+
+
+@pytest.mark.parametrize("n_tiles,bh_count,grid", [(32, 128, 512), (32, 64, 512), (16, 128, 504), (8, 48, 64),
+                                                   (5, 6, 16), (8, 256, 512)])
+def test_persistent_assignment_xcd_order(n_tiles, bh_count, grid):
+    """The order for grids of several rounds: every tile exactly once, each
+    work-group on its XCD's pairs, and the items in flight on an XCD in any round
+    spanning few pairs (the L2 sharing the order is for)."""
+    items = _kernel_items(n_tiles, bh_count, grid, xcd_order=True)
+    seen = [x for g in items for x in items[g]]
+    assert sorted(seen) == sorted((bh, t) for bh in range(bh_count) for t in range(n_tiles))
+    if bh_count % 8 == 0 and grid % 8 == 0:
+        for g, lst in items.items():
+            assert all(bh % 8 == g % 8 for bh, _ in lst)
+        # round r's items on XCD x: grid / 8 consecutive items of that XCD's
+        # sequence, i.e. at most ceil(grid / 8 / n_tiles) + 1 pairs
+        rounds = max(len(lst) for lst in items.values())
+        for r in range(rounds):
+            for x in range(8):
+                pairs = {lst[r][0] for g, lst in items.items() if g % 8 == x and r < len(lst)}
+                assert len(pairs) <= -(-(grid // 8) // n_tiles) + 1
+    # each pair's tiles reach a work-group longest first
+    for lst in items.values():
+        by_pair = {}
+        for bh, t in lst:
+            by_pair.setdefault(bh, []).append(t)
+        assert all(ts == sorted(ts, reverse=True) for ts in by_pair.values())
 
 
 SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle", "schedule.py")
