@@ -98,6 +98,36 @@ int launch_fwd(const AttnParams& p, int d, int causal, hipStream_t s) {
     return d == 64 ? launch_fwd_d<64, VARLEN>(p, causal, s) : launch_fwd_d<128, VARLEN>(p, causal, s);
 }
 
+// Work-group slots of the current device: every kernel here runs 2 work-groups
+// per CU.
+int fwd_slots(int* slots) {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        return FA_ERR_LAUNCH;
+    *slots = 2 * cus;
+    return FA_OK;
+}
+
+// Grid of a backward pass with `items` work items: one work-group per item, or,
+// for dense causal passes of more than one and at most four rounds of the
+// work-group slots, a persistent grid of one work-group per slot (rounded down
+// to a multiple of 8) that deals the items itself.  Measured on MI355X
+// (alternating, bitwise the same gradients): B8 H16 N2048 d128 causal dK/dV
+// 0.293 against 0.323 ms and dQ 0.236 against 0.262 ms, B4 H16 N4096 5% and 4%
+// faster; at eight rounds (B8 H16 N4096) 0.5-1% slower, on the long context
+// (B1 H16 N32768) 4% slower, non-causal 3-4% slower.
+template <bool VARLEN>
+int bwd_grid(int64_t items, int causal, int* grid) {
+    int slots = 0;
+    const int st = fwd_slots(&slots);
+    if (st) return st;
+    if (items > INT_MAX) return FA_ERR_SHAPE;
+    *grid = (int)items;
+    if (!VARLEN && causal && items > slots && items <= 4 * (int64_t)slots) *grid = slots / 8 * 8;
+    return FA_OK;
+}
+
 // Backward stages.  `p.n_tiles` is set per stage from the stage's own tiling.
 template <int D, bool VARLEN>
 int launch_bwd_dot_d(AttnParams p, hipStream_t s) {
@@ -110,7 +140,10 @@ template <int D, bool VARLEN>
 int launch_bwd_dkdv_d(AttnParams p, int causal, hipStream_t s) {
     using KV = BwdKVCfg<D>;
     p.n_tiles = (p.nk + KV::BN - 1) / KV::BN;
-    const int grid = p.n_tiles * p.H * p.batch;
+    int grid = 0;
+    const int st = bwd_grid<VARLEN>((int64_t)p.n_tiles * p.H * p.batch, causal, &grid);
+    if (st) return st;
+    if (!VARLEN && grid < p.n_tiles * p.H * p.batch) return launch(fa_bwd_dkdv_persistent_kernel<D>, grid, KV::NW * 64, s, p);
     return causal ? launch(fa_bwd_dkdv_kernel<D, true, VARLEN>, grid, KV::NW * 64, s, p)
                   : launch(fa_bwd_dkdv_kernel<D, false, VARLEN>, grid, KV::NW * 64, s, p);
 }
@@ -119,19 +152,12 @@ template <int D, bool VARLEN, bool DOT>
 int launch_bwd_dq_d(AttnParams p, int causal, hipStream_t s) {
     using Q = BwdQCfg<D>;
     p.n_tiles = (p.nq + Q::BM - 1) / Q::BM;
-    const int grid = p.n_tiles * p.H * p.batch;
+    int grid = 0;
+    const int st = bwd_grid<VARLEN>((int64_t)p.n_tiles * p.H * p.batch, causal, &grid);
+    if (st) return st;
+    if (!VARLEN && grid < p.n_tiles * p.H * p.batch) return launch(fa_bwd_dq_persistent_kernel<D, DOT>, grid, Q::NW * 64, s, p);
     return causal ? launch(fa_bwd_dq_kernel<D, true, VARLEN, DOT>, grid, Q::NW * 64, s, p)
                   : launch(fa_bwd_dq_kernel<D, false, VARLEN, DOT>, grid, Q::NW * 64, s, p);
-}
-
-// Work-group slots of the current device: 2 forward work-groups per CU.
-int fwd_slots(int* slots) {
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-        return FA_ERR_LAUNCH;
-    *slots = 2 * cus;
-    return FA_OK;
 }
 
 template <int D>

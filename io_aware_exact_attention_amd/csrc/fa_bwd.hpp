@@ -137,8 +137,12 @@ template <int D, bool CAUSAL, bool VARLEN>
 __device__ __forceinline__ void dkdv_item(const AttnParams& p, char* smem, int bh, int tile) {
     using C = BwdKVCfg<D>;
 
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: scalar branches
+    // (opaque to the optimiser: in a persistent loop, offsets derived from the
+    // lane are recomputed per item instead of being held live across items)
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar branches
     const int h2 = lane >> 5;
     const int col = lane & 31;
     const int sl = lane & 15;
@@ -332,6 +336,22 @@ void fa_bwd_dkdv_kernel(AttnParams p) {
     dkdv_item<D, CAUSAL, VARLEN>(p, smem, bh, tile);
 }
 
+// The same pass for dense causal grids of a few rounds, on a persistent grid of
+// two work-groups per CU dealing the same items in the same order: a work-group
+// that drew a short (high) key tile takes the next one at once instead of
+// leaving its slot to the hardware's dispatcher.  Same item arithmetic, so the
+// same gradients bit for bit.
+template <int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void fa_bwd_dkdv_persistent_kernel(AttnParams p) {
+    __shared__ __attribute__((aligned(1024))) char smem[BwdKVCfg<D>::LDS_BYTES];
+    persistent_items(p.n_tiles * p.H * p.batch, [&](int it) {
+        int bh, tile;
+        xcd_work_item(it, p.n_tiles, p.H * p.batch, bh, tile);
+        dkdv_item<D, true, false>(p, smem, bh, tile);
+    });
+}
+
 // ---------------------------------------------------------------------------
 // 3. dQ (query-tile outer).  With DOT it first computes D_i = rowsum(dO * O) of
 // its own rows (kernel 1's products, summed in kernel 1's pairwise order, so the
@@ -344,8 +364,10 @@ template <int D, bool CAUSAL, bool VARLEN, bool DOT>
 __device__ __forceinline__ void dq_item(const AttnParams& p, char* smem, int bh, int tile) {
     using C = BwdQCfg<D>;
 
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    int tid = threadIdx.x;   // (opaque, as in dkdv_item)
+    asm volatile("" : "+v"(tid));
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
     const int h2 = lane >> 5;
     const int col = lane & 31;
     const int sl = lane & 15;
@@ -552,6 +574,18 @@ void fa_bwd_dq_kernel(AttnParams p) {
     int bh, rank;   // longest causal rows first
     xcd_work_item(blockIdx.x, p.n_tiles, p.H * p.batch, bh, rank);
     dq_item<D, CAUSAL, VARLEN, DOT>(p, smem, bh, p.n_tiles - 1 - rank);
+}
+
+// The same pass on a persistent grid, as fa_bwd_dkdv_persistent_kernel.
+template <int D, bool DOT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void fa_bwd_dq_persistent_kernel(AttnParams p) {
+    __shared__ __attribute__((aligned(1024))) char smem[BwdQCfg<D>::LDS_BYTES];
+    persistent_items(p.n_tiles * p.H * p.batch, [&](int it) {
+        int bh, rank;
+        xcd_work_item(it, p.n_tiles, p.H * p.batch, bh, rank);
+        dq_item<D, true, false, DOT>(p, smem, bh, p.n_tiles - 1 - rank);
+    });
 }
 
 // ---------------------------------------------------------------------------

@@ -170,4 +170,24 @@ __device__ __forceinline__ void lpt_work_item(int id, int n_tiles, int bh_count,
     rank = id / bh_count;
 }
 
+// Items 0 .. total-1 of a persistent grid (a multiple of 8 work-groups): rounds
+// of one item per work-group, even rounds in work-group order and odd rounds
+// with each XCD's work-groups reversed, so that a work-group's items in
+// longest-first order sum to about the same on every work-group.  Calls
+// run(item) with a wave-uniform item, separated by a barrier because the next
+// item reuses the LDS.
+template <typename F>
+__device__ __forceinline__ void persistent_items(int total, F&& run) {
+    const int grid = gridDim.x;
+    const int g = blockIdx.x;
+    const int g_rev = 8 * ((grid >> 3) - 1 - (g >> 3)) + (g & 7);   // same XCD, reversed
+#pragma unroll 1
+    for (int base = 0, r = 0; base < total; base += grid, ++r) {
+        const int it = __builtin_amdgcn_readfirstlane(base + ((r & 1) ? g_rev : g));
+        if (it >= total) continue;
+        run(it);
+        if (base + grid < total) __syncthreads();
+    }
+}
+
 }  // namespace fa355

@@ -106,6 +106,18 @@ def bwd_is_fused(B, H, Nq, Nk, causal) -> bool:
     return (-(-Nk // 128) + -(-Nq // 128)) * B * H <= (8 if causal else 2) * cus
 
 
+def bwd_is_persistent(B, H, Nq, Nk, causal) -> bool:
+    """Whether fa_bwd runs its dK/dV (128-key tiles) and dQ (128-row tiles) passes
+    on persistent grids: dense causal backwards that do not take the one-launch
+    form, for each pass that has more work items than two per CU and at most
+    eight (returns the dK/dV pass's answer, then the dQ pass's)."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    if not causal or bwd_is_fused(B, H, Nq, Nk, causal):
+        return False, False
+    items = (-(-Nk // 128) * B * H, -(-Nq // 128) * B * H)
+    return tuple(2 * cus < n <= 8 * cus for n in items)
+
+
 def run_dense(x, scale, causal, backward=True):
     """x: dict of CPU bf16 tensors q, k, v (dout); returns GPU results on the host."""
     dev = torch.device("cuda", 0)

@@ -23,7 +23,7 @@ from io_aware_exact_attention_amd import build as fa_build
 
 # kernels whose schedules assume two waves per SIMD
 TWO_WAVE_KERNELS = ("fa_fwd_kernel", "fa_fwd_persistent_kernel", "fa_fwd_split_kernel", "fa_bwd_dq_kernel", "fa_bwd_dkdv_kernel",
-                    "fa_bwd_fused_kernel")
+                    "fa_bwd_fused_kernel", "fa_bwd_dq_persistent_kernel", "fa_bwd_dkdv_persistent_kernel")
 
 
 def _remarks():

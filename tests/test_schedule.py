@@ -48,7 +48,8 @@ def test_lpt_within_grahams_bound(seed):
 
 
 def _kernel_items(n_tiles, bh_count, grid, xcd_order=False):
-    """The persistent forward kernel's assignment, restated: the items, numbered
+    """The persistent forward kernel's assignment (with xcd_order also the
+    persistent backward kernels', whose dK/dV pass takes tile = rank), restated: the items, numbered
     longest first over all pairs (item i -> (pair, rank), pairs dealt over the 8
     XCDs) or, with xcd_order, pair by pair per XCD (the per-tile kernel's order),
     are dealt in rounds of one per work-group, even rounds in work-group order,
