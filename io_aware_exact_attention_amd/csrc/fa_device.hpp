@@ -106,7 +106,13 @@ __device__ __forceinline__ void global_to_lds16(const void* g, FA_LDS void* lds_
     __builtin_amdgcn_global_load_lds(g, lds_wave_base, 16, 0, 0);
 }
 
-__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maxima: gfx9 encoding),
+// through the builtin so that the compiler's own bookkeeping of outstanding
+// loads sees it, then a compiler barrier for the LDS accesses that follow.
+__device__ __forceinline__ void wait_vmem() {
+    __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
+    asm volatile("" ::: "memory");
+}
 
 __device__ __forceinline__ bf16x8 lds_read16(const FA_LDS char* p) {
     return *reinterpret_cast<const FA_LDS bf16x8*>(p);

@@ -248,17 +248,14 @@ struct Fp8TileLoader {
             voff[i] = r * row_bytes + 16 * lc;
         }
     }
+    // (compiler-invisible direct-to-LDS loads, as TileLoader's: the kernel waits
+    // for them explicitly before reading the tile)
     __device__ __forceinline__ void load(FA_LDS char* lds_tile, const void* base, uint32_t bytes,
                                          int first_bytes, int wave) const {
-#if defined(__HIP_DEVICE_COMPILE__)
-        const auto rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
-                                                            (int)bytes, 0x00020000);
+        const u32x4 rsrc = raw_rsrc(base, bytes);
 #pragma unroll
         for (int i = 0; i < Fp8Cfg::INSTS; ++i)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rsrc, (FA_LDS void*)(lds_tile + (wave * Fp8Cfg::INSTS + i) * 1024), 16, voff[i],
-                first_bytes, 0, 0);
-#endif
+            dma_lds16(rsrc, (FA_LDS void*)(lds_tile + (wave * Fp8Cfg::INSTS + i) * 1024), voff[i], first_bytes);
     }
 };
 

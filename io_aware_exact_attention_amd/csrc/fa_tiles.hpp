@@ -14,6 +14,48 @@ namespace fa355 {
 // consecutive rows (from a multiple of 4) at 4 adjacent chunks, 64 bytes each
 // (transposed operands).  The XOR below makes (a) a permutation of the 16 chunk
 // slots and sends the 4 rows of (b) to 4 different 64-byte bank groups.
+// Direct HBM->LDS loads issued as inline assembly, so that the compiler does not
+// see them.  The compiler cannot tell which LDS bytes a direct-to-LDS load
+// writes, so for the ones it sees it makes LDS reads wait for all of them
+// (s_waitcnt vmcnt(0)): in the forward's key loop that put a wait for the next
+// tiles' loads, issued at the top of the iteration, in front of the current V
+// tile's reads, in the middle of the iteration.  Every caller here waits for its
+// loads explicitly (s_waitcnt vmcnt(0) and a barrier) before reading what they
+// load, and issues them only after a barrier that ends all reads of the bytes
+// they overwrite.  Lane l's `size` bytes at base + voff + soff land at
+// lds + size * l, through a raw buffer resource (gfx9-family word 3) whose range
+// ends at `bytes`: reads past it return zeros and touch no memory.  M0 carries
+// the LDS address and is restored afterwards; the load writes no VGPR.
+// (base and bytes are wave-uniform; the SGPR operand needs them in scalar registers)
+__device__ __forceinline__ u32x4 raw_rsrc(const void* base, uint32_t bytes) {
+    const uint64_t b = reinterpret_cast<uint64_t>(base);
+    return (u32x4){(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b),
+                   (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32) & 0xffffu),
+                   (uint32_t)__builtin_amdgcn_readfirstlane(bytes), 0x00020000u};
+}
+
+__device__ __forceinline__ void dma_lds16(const u32x4& rsrc, FA_LDS void* lds, int voff, int soff) {
+    const uint32_t l = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+        "buffer_load_dwordx4 %2, %3, %4 offen lds\n\ts_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(l), "v"(voff), "s"(rsrc), "s"(soff)
+        : "memory");
+}
+
+__device__ __forceinline__ void dma_lds4(const u32x4& rsrc, FA_LDS void* lds, int voff, int soff) {
+    const uint32_t l = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+        "buffer_load_dword %2, %3, %4 offen lds\n\ts_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(l), "v"(voff), "s"(rsrc), "s"(soff)
+        : "memory");
+}
+
 template <int D>
 __device__ __forceinline__ int tile_swz(int row) {
     if constexpr (D == 128) return 4 * (row & 3) + ((row >> 2) & 3);
@@ -84,21 +126,13 @@ struct TileLoader {
 
     // Rows [first, first + ROWS) of the tensor starting at `base`, whose valid
     // rows span `bytes` bytes; `first_bytes` = first * row_bytes (wave-uniform).
-    // The loads go through a raw buffer resource (gfx9-family word 3) whose range
-    // ends at `bytes`: rows past it read as zeros and touch no memory.
+    // Rows past `bytes` read as zeros and touch no memory (dma_lds16).
     __device__ __forceinline__ void load(FA_LDS char* lds_tile, const void* base, uint32_t bytes,
                                          int first_bytes, int wave) const {
-#if defined(__HIP_DEVICE_COMPILE__)
-        // (the resource type exists only for the device; keeping it out of the
-        // host pass also keeps clang emitting every kernel instantiation's stub)
-        const auto rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
-                                                            (int)bytes, 0x00020000);
+        const u32x4 rsrc = raw_rsrc(base, bytes);
 #pragma unroll
         for (int i = 0; i < INSTS; ++i)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rsrc, (FA_LDS void*)(lds_tile + (wave * INSTS + i) * 1024), 16, voff[i],
-                first_bytes, 0, 0);
-#endif
+            dma_lds16(rsrc, (FA_LDS void*)(lds_tile + (wave * INSTS + i) * 1024), voff[i], first_bytes);
     }
 };
 
@@ -145,12 +179,7 @@ constexpr int kRowSliceBytes = 32 * (D * 2 + 16);   // one wave's slice for stor
 // past it read as zeros.  `first_bytes` = 4 * first (wave-uniform).
 __device__ __forceinline__ void load_f32x64_lds(FA_LDS char* lds, const float* base, uint32_t bytes,
                                                 int first_bytes) {
-#if defined(__HIP_DEVICE_COMPILE__)
-    const auto rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), (short)0,
-                                                        (int)bytes, 0x00020000);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (FA_LDS void*)lds, 4, lane_x4_here(), first_bytes,
-                                             0, 0);
-#endif
+    dma_lds4(raw_rsrc(base, bytes), (FA_LDS void*)lds, lane_x4_here(), first_bytes);
 }
 
 }  // namespace fa355
