@@ -76,13 +76,46 @@ struct FwdCfg {
 // half's (m, l, lr, O) go through LDS to the wave of the first half that holds the
 // same query rows, which combines the two online-softmax states exactly as a new
 // tile would (scale each by e^(m_half - m_max), add) and writes the output.
-template <int D, bool CAUSAL, bool VARLEN, int SPLIT = 1>
-__device__ __forceinline__ void fwd_tile(const AttnParams& p, char* smem, int bh, int tile) {
+//
+// CARRY = true (dense, one key range; the persistent kernel's multi-round
+// form): consecutive items of a work-group overlap.  After its key loop an item
+// issues the next item's first K, V and second K tiles (into the first three
+// 16 KB tiles of the LDS) before its own epilogue, which goes through row
+// slices above them (3 * 16 KB on, within the 16 KB the kernel adds to the K/V
+// buffers); once a wave has read its slice back it loads the next item's Q rows
+// for that wave into the same slice, then issues a fixed number of buffer
+// stores.  The next item (nx.pre) waits only for those loads, leaving the stores
+// outstanding, and reads its Q fragments from the slice.  All these loads go
+// straight to LDS, so the compiler's bookkeeping of register loads never spans
+// two items.
+struct FwdNext {
+    bool pre;    // this item's Q and first tiles were issued by the previous item
+    bool has;    // there is a next item: (bh, tile)
+    int bh, tile;
+};
+
+template <int D>
+constexpr int kCarrySliceOff = 3 * FwdCfg<D>::TILE_BYTES;
+template <int D>
+constexpr int kCarryLdsBytes = FwdCfg<D>::LDS_BYTES + 16384;
+template <int D>
+constexpr int kCarryStores = 32 / (64 / (D / 8)) + 1;   // O row stores + the LSE store, per wave
+
+template <int D, bool CAUSAL, bool VARLEN, int SPLIT, bool CARRY>
+__device__ __forceinline__ void fwd_tile(const AttnParams& p, char* smem, int bh, int tile, const FwdNext& nx) {
     using C = FwdCfg<D, SPLIT == 2 ? 64 : FwdCfg<D>::BN>;
     static_assert(SPLIT == 1 || SPLIT == 2, "one or two key halves");
-    const int lane = threadIdx.x & 63;
-    const int wave = (threadIdx.x >> 6) & (C::NW - 1);   // row block of this wave
-    const int half = SPLIT == 2 ? (threadIdx.x >> 6) / C::NW : 0;
+    static_assert(!CARRY || (SPLIT == 1 && !VARLEN), "carried items: dense, one key range");
+    static_assert(!CARRY || kCarrySliceOff<D> + C::NW * 32 * 2 * D <= kCarryLdsBytes<D>, "slices fit");
+    // (wave-uniform: scalar branches, which the compiler's wait bookkeeping follows)
+    const bool pre = CARRY && __builtin_amdgcn_readfirstlane((int)nx.pre) != 0;
+    // (carried items run in a loop: opaque to the optimiser, so that offsets
+    // derived from the lane are recomputed per item instead of held across items)
+    int tid = threadIdx.x;
+    if constexpr (CARRY) asm volatile("" : "+v"(tid));
+    const int lane = tid & 63;
+    const int wave = (tid >> 6) & (C::NW - 1);   // row block of this wave
+    const int half = SPLIT == 2 ? (tid >> 6) / C::NW : 0;
     const int h2 = lane >> 5;
     const int col = lane & 31;
     const int sl = lane & 15;
@@ -132,10 +165,22 @@ __device__ __forceinline__ void fwd_tile(const AttnParams& p, char* smem, int bh
     // 1.90 ms on B8 H16 N4096 instead of 1.10 ms.  Behind the asm every forward
     // variant fits in 223 registers with no scratch.
     asm volatile("" : "+v"(n_w));
-    const bf16* qptr = p.q + (int64_t)(qs + min(qi, nq - 1)) * tok + h * D + 8 * h2;
     bf16x8 qf[C::KSTEPS];
+    if constexpr (CARRY) {
+        // (carried items take Q through this wave's slice of the LDS, rows past
+        // nq as zeros: below; the first item of a work-group loads it there too,
+        // so that no Q fragment register is ever the target of a memory load
+        // whose wait the compiler would place inside the key loop)
+        if (!pre) {
+            const TileLoader<D, C::BM, C::NW> qload(row_bytes, wave, lane);
+            qload.load((FA_LDS char*)smem + kCarrySliceOff<D>, p.q + (int64_t)qs * tok + h * D,
+                       (uint32_t)nq * row_bytes, q_start * row_bytes, wave_s);
+        }
+    } else {
+        const bf16* qptr = p.q + (int64_t)(qs + min(qi, nq - 1)) * tok + h * D + 8 * h2;
 #pragma unroll
-    for (int s = 0; s < C::KSTEPS; ++s) qf[s] = load16(qptr + 16 * s);
+        for (int s = 0; s < C::KSTEPS; ++s) qf[s] = load16(qptr + 16 * s);
+    }
 
     f32x16 acc[C::DBLK];
 #pragma unroll
@@ -151,11 +196,23 @@ __device__ __forceinline__ void fwd_tile(const AttnParams& p, char* smem, int bh
 
     // LDS: buffer j (j = 0, 1) holds a K tile at 2 j TILE_BYTES and a V tile
     // TILE_BYTES after it.  K(t) sits in buffer t % 2, V(t) in buffer t % 2.
-    if (n_kv > 0) {
-        loader.load(ldsb, kbase, kv_bytes, 0, wave_s);
-        loader.load(ldsb + C::TILE_BYTES, vbase, kv_bytes, 0, wave_s);
+    if (!pre) {
+        if (n_kv > 0) {
+            loader.load(ldsb, kbase, kv_bytes, 0, wave_s);
+            loader.load(ldsb + C::TILE_BYTES, vbase, kv_bytes, 0, wave_s);
+        }
+        if (n_kv > 1) loader.load(ldsb + 2 * C::TILE_BYTES, kbase, kv_bytes, C::BN * row_bytes, wave_s);
+        wait_vmem();
+    } else {
+        // (a carried item: its loads were issued before the previous item's
+        // kCarryStores<D> stores, which may stay in flight)
+        wait_vmcnt<kCarryStores<D>>();
     }
-    if (n_kv > 1) loader.load(ldsb + 2 * C::TILE_BYTES, kbase, kv_bytes, C::BN * row_bytes, wave_s);
+    if constexpr (CARRY) {   // this wave's Q rows, from its own slice
+        const FA_LDS char* qt = (const FA_LDS char*)smem + kCarrySliceOff<D>;
+#pragma unroll
+        for (int s = 0; s < C::KSTEPS; ++s) qf[s] = lds_read16(qt + tile_off<D>(wave * 32 + col, 2 * s + h2));
+    }
 
     // per-lane byte offsets of the K operand reads (one per k-step) within a tile
     int koff[C::KSTEPS];
@@ -249,7 +306,6 @@ __device__ __forceinline__ void fwd_tile(const AttnParams& p, char* smem, int bh
     };
 
     f32x16 s[C::KB];   // scores of the tile the loop is at
-    wait_vmem();
     __syncthreads();
     if (n_w > 0) {
         scores(ldsb, s);
@@ -263,7 +319,12 @@ __device__ __forceinline__ void fwd_tile(const AttnParams& p, char* smem, int bh
         constexpr int PB = decltype(par)::value;   // t % 2
         const FA_LDS char* k_next = ldsb + (1 - PB) * 2 * C::TILE_BYTES;   // K(t+1)
         const FA_LDS char* v_cur = ldsb + PB * 2 * C::TILE_BYTES + C::TILE_BYTES;   // V(t)
-        wait_vmem();
+        // (iteration 0 of a carried item: only the previous item's stores can
+        // be in flight)
+        if (CARRY && pre && t == 0)
+            wait_vmcnt<kCarryStores<D>>();
+        else
+            wait_vmem();
         __syncthreads();
         if (t + 2 < n_kv)   // K(t+2) replaces K(t), whose scores every wave has formed
             loader.load(ldsb + PB * 2 * C::TILE_BYTES, kbase, kv_bytes, (t + 2) * C::BN * row_bytes, wave_s);
@@ -343,6 +404,45 @@ __device__ __forceinline__ void fwd_tile(const AttnParams& p, char* smem, int bh
     const float lt = sum_halves(l);
     const float lrt = sum_halves(lr);
     const float inv = lrt > 0.f ? 1.f / lrt : 0.f;
+    if constexpr (CARRY) {
+        __syncthreads();   // every wave is done with the K/V buffers
+        const bool has = __builtin_amdgcn_readfirstlane((int)nx.has) != 0;
+        const bf16* qb_n = p.q;
+        uint32_t qbytes_n = 0;
+        int qfirst_n = 0;
+        if (has) {   // the next item's first three K/V tiles
+            const int hn = nx.bh % p.H;
+            const int bn = nx.bh / p.H;
+            int qs_n, nq_n, ks_n, nk_n;
+            seq_range<false>(p, bn, qs_n, nq_n, ks_n, nk_n);
+            const int q_start_n = nx.tile * C::BM;
+            const int kv_end_n = CAUSAL ? min(nk_n, q_start_n + C::BM) : nk_n;
+            const bf16* kb_n = p.k + (int64_t)ks_n * tok + hn * D;
+            const bf16* vb_n = p.v + (int64_t)ks_n * tok + hn * D;
+            const uint32_t kvb_n = (uint32_t)nk_n * row_bytes;
+            loader.load(ldsb, kb_n, kvb_n, 0, wave_s);
+            loader.load(ldsb + C::TILE_BYTES, vb_n, kvb_n, 0, wave_s);
+            if (kv_end_n > C::BN) loader.load(ldsb + 2 * C::TILE_BYTES, kb_n, kvb_n, C::BN * row_bytes, wave_s);
+            qb_n = p.q + (int64_t)qs_n * tok + hn * D;
+            qbytes_n = (uint32_t)nq_n * row_bytes;
+            qfirst_n = q_start_n * row_bytes;
+        }
+        // O (through this wave's slice), then LSE: kCarryStores<D> store
+        // instructions per wave; between reading the slice back and the stores,
+        // the next item's Q rows of this wave go into the slice
+        FA_LDS char* slice = (FA_LDS char*)smem + kCarrySliceOff<D> + wave * 32 * 2 * D;
+        store_rows_fixed<D>(slice, acc, inv, p.o + (int64_t)qs * tok + h * D,
+                            (uint32_t)(nq - 1) * row_bytes + 2 * D, row_bytes, qw0, lane, [&]() {
+            if (has) {
+                wait_lgkmcnt0();   // this wave's slice reads are done
+                const TileLoader<D, C::BM, C::NW> qload(row_bytes, wave, lane);
+                qload.load((FA_LDS char*)smem + kCarrySliceOff<D>, qb_n, qbytes_n, qfirst_n, wave_s);
+            }
+        });
+        store_f32_fixed(p.lse + ((int64_t)b * p.H + h) * p.nq, (uint32_t)nq * 4, h2 ? 0x7ffffff0 : 4 * qi,
+                        lt > 0.f ? (m * c + __builtin_amdgcn_logf(lt)) * kLn2 : kNegInf);
+        return;
+    }
     if constexpr (SPLIT == 1) {
         // O through LDS, stored back as whole 16-byte chunks (bitwise the same
         // output; 0.3-3% faster than 8-byte stores of 32 rows each)
@@ -368,6 +468,11 @@ __device__ __forceinline__ void fwd_tile(const AttnParams& p, char* smem, int bh
                 lt > 0.f ? (m * c + __builtin_amdgcn_logf(lt)) * kLn2 : kNegInf;
         }
     }
+}
+
+template <int D, bool CAUSAL, bool VARLEN, int SPLIT = 1>
+__device__ __forceinline__ void fwd_tile(const AttnParams& p, char* smem, int bh, int tile) {
+    fwd_tile<D, CAUSAL, VARLEN, SPLIT, false>(p, smem, bh, tile, FwdNext{false, false, 0, 0});
 }
 
 // One work-group per query tile, in the order xcd_work_item gives.
@@ -419,21 +524,38 @@ void fa_fwd_split_kernel(AttnParams p) {
 template <int D, bool CAUSAL, bool XCD_ORDER>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fa_fwd_persistent_kernel(AttnParams p) {
-    __shared__ __attribute__((aligned(1024))) char smem[FwdCfg<D>::LDS_BYTES];
+    // The multi-round form at d = 128 carries each item's successor (16 KB more
+    // LDS).  Measured on MI355X, alternating, bitwise the same output: B16 H16
+    // N1024 5% faster, B8 H16 N2048 2%, B4 H16 N4096 and B2 H32 N8192 0.6%, the
+    // headline B8 H16 N4096 and the long context within 0.7% either way; at
+    // d = 64 (B8 H16 N4096) 1.6% slower, so not there.
+    constexpr bool CARRY = XCD_ORDER && D == 128;
+    __shared__ __attribute__((aligned(1024))) char smem[CARRY ? kCarryLdsBytes<D> : FwdCfg<D>::LDS_BYTES];
     const int bh_count = p.H * p.batch;
     const int total = p.n_tiles * bh_count;
     const int grid = gridDim.x;   // a multiple of 8
     const int g = blockIdx.x;
     const int g_rev = 8 * ((grid >> 3) - 1 - (g >> 3)) + (g & 7);   // same XCD, reversed
-    for (int base = 0, r = 0; base < total; base += grid, ++r) {
-        const int it = base + ((r & 1) ? g_rev : g);
-        if (it >= total) continue;
-        int bh, rank;
+    auto item = [&](int it, int& bh, int& tile) {
+        int rank;
         if constexpr (XCD_ORDER)
             xcd_work_item(it, p.n_tiles, bh_count, bh, rank);
         else
             lpt_work_item(it, p.n_tiles, bh_count, bh, rank);
-        fwd_tile<D, CAUSAL, false>(p, smem, bh, p.n_tiles - 1 - rank);
+        tile = p.n_tiles - 1 - rank;
+    };
+    FwdNext nx{false, false, 0, 0};
+    for (int base = 0, r = 0; base < total; base += grid, ++r) {
+        const int it = base + ((r & 1) ? g_rev : g);
+        if (it >= total) continue;   // (only in the last round)
+        int bh, tile;
+        item(it, bh, tile);
+        // this work-group's next item: the next round's (rounds alternate direction)
+        const int it_next = base + grid + ((r & 1) ? g : g_rev);
+        nx.has = CARRY && it_next < total;
+        if (nx.has) item(it_next, nx.bh, nx.tile);
+        fwd_tile<D, CAUSAL, false, 1, CARRY>(p, smem, bh, tile, nx);
+        nx.pre = nx.has;
         __syncthreads();   // the next item's loads reuse the LDS buffers
     }
 }

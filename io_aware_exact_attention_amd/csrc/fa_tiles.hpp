@@ -174,6 +174,77 @@ __device__ __forceinline__ void store_rows_via_lds(FA_LDS char* slice, const f32
 template <int D>
 constexpr int kRowSliceBytes = 32 * (D * 2 + 16);   // one wave's slice for store_rows_via_lds
 
+// store_rows_via_lds with a fixed number of store instructions: the rows sit
+// unpadded in the slice (32 * 2D bytes) with their 16-byte chunks XOR-permuted
+// by the row (as conflict-free as the padding), and every store is issued, as a
+// buffer store through `rsrc`, whose range ends at the last valid row's D values
+// so that the hardware drops the rows past it.  Each wave issues exactly
+// 32 / (64 / (D / 8)) store instructions, so that a later s_waitcnt can leave
+// them outstanding and wait only for loads issued before them.  Row i goes to
+// byte offset (row0 + i) * row_bytes of the resource.
+// `between()` runs after the slice has been read back (the reads may still be
+// in flight) and before the stores.
+template <int D, typename F>
+__device__ __forceinline__ void store_rows_fixed(FA_LDS char* slice, const f32x16 (&acc)[D / 32], float mul,
+                                                 const void* base, uint32_t bytes, int row_bytes, int row0,
+                                                 int lane, F&& between) {
+    constexpr int RS = D * 2;
+    constexpr int CPRW = D / 8;
+    constexpr int RPI = 64 / CPRW;
+    const int col = lane & 31;
+    const int h2 = lane >> 5;
+#pragma unroll
+    for (int cb = 0; cb < D / 32; ++cb)
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+            const u32x2 u = (u32x2){pack_bf16x2(acc[cb][4 * rg] * mul, acc[cb][4 * rg + 1] * mul),
+                                    pack_bf16x2(acc[cb][4 * rg + 2] * mul, acc[cb][4 * rg + 3] * mul)};
+            const int chunk = (cb * 4 + rg) ^ (col & (CPRW - 1));
+            *reinterpret_cast<FA_LDS u32x2*>(slice + col * RS + 16 * chunk + 8 * h2) = u;
+        }
+    const int rr = lane / CPRW;
+    const int ch = lane % CPRW;
+    u32x4 v4[32 / RPI];
+#pragma unroll
+    for (int i = 0; i < 32 / RPI; ++i) {
+        const int row = i * RPI + rr;
+        v4[i] = *reinterpret_cast<const FA_LDS u32x4*>(slice + row * RS + 16 * (ch ^ (row & (CPRW - 1))));
+    }
+    between();
+#if defined(__HIP_DEVICE_COMPILE__)
+    const auto rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                                        0x00020000);
+#pragma unroll
+    for (int i = 0; i < 32 / RPI; ++i)
+        __builtin_amdgcn_raw_buffer_store_b128(v4[i], rsrc, (row0 + i * RPI + rr) * row_bytes + 16 * ch, 0, 0);
+#endif
+}
+
+// One fp32 per lane at byte offset `off` of a resource of `bytes` bytes from
+// `base` (dropped by the hardware when off >= bytes): one store instruction.
+__device__ __forceinline__ void store_f32_fixed(const float* base, uint32_t bytes, int off, float v) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    const auto rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), (short)0, (int)bytes,
+                                                        0x00020000);
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rsrc, off, 0, 0);
+#endif
+}
+
+// s_waitcnt lgkmcnt(0), the other counters at their maxima (gfx9 encoding).
+__device__ __forceinline__ void wait_lgkmcnt0() {
+    __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));
+    asm volatile("" ::: "memory");
+}
+
+// s_waitcnt vmcnt(N), the other counters at their maxima (gfx9 encoding),
+// through the builtin so that the compiler's bookkeeping of loads sees it.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit field");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+    asm volatile("" ::: "memory");
+}
+
 // 64 consecutive fp32 values base[first..first+63] into LDS (one per lane, in
 // lane order), through a buffer resource whose range ends at `bytes`: values
 // past it read as zeros.  `first_bytes` = 4 * first (wave-uniform).
