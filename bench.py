@@ -474,6 +474,21 @@ def fa_fwd_kernel_name(B: int, H: int, N: int, causal: bool) -> str:
     return "fa_fwd_kernel"
 
 
+def fa_bwd_pass_kernel_names(B: int, H: int, N: int, causal: bool) -> tuple:
+    """The kernels fa_bwd_dq_dot and fa_bwd_dkdv launch for a dense shape (their
+    documented choice): each pass on a persistent grid when causal with more
+    than two 128-row tiles per CU and either at most eight per CU, or at most 32
+    tiles per sequence with items times tiles per sequence at most 512 per CU;
+    else one work-group per tile."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    t = -(-N // 128)
+    items = t * B * H
+    pers = causal and items > 2 * cus and (items <= 8 * cus or (t <= 32 and items * t <= 512 * cus))
+    if pers:
+        return "fa_bwd_dq_persistent_kernel", "fa_bwd_dkdv_persistent_kernel"
+    return "fa_bwd_dq_kernel", "fa_bwd_dkdv_kernel"
+
+
 def fa_bwd_is_fused(B: int, H: int, N: int, causal: bool) -> bool:
     """Whether fa_bwd runs as the row-dot kernel and one launch holding both
     passes (its documented choice for small dense grids: at most 8 causal or 2
@@ -561,7 +576,7 @@ def main():
     persistent = args.forward == "persistent"
     fused = fa_bwd_is_fused(B, H, N, causal)
     names = ["fa_fwd_persistent_kernel" if persistent else fa_fwd_kernel_name(B, H, N, causal),
-             "fa_bwd_dq_kernel", "fa_bwd_dkdv_kernel"]
+             *fa_bwd_pass_kernel_names(B, H, N, causal)]
     fwd = fa355.fa_fwd_persistent if persistent else fa355.fa_fwd
     calls = [   # fa_bwd = fa_bwd_dq_dot, then fa_bwd_dkdv (one kernel each)
         lambda: fwd(q, k, v, o, lse, scale, causal),

@@ -137,9 +137,11 @@ size_t fa_bwd_workspace_bytes(int batch_or_nseq, int H, int nq, int d);
  * causal or 2 non-causal dK/dV plus dQ tiles of 128 rows per CU) fa_bwd_dot's
  * kernel, then one launch holding both passes' tiles, so that each pass's causal
  * tail overlaps the other's work ("LLM Systems 22: Flash Attention", §4.1.5
- * load balancing).  Causal passes of more than 2 and at most 8 tiles per CU
- * run on a persistent grid of two work-groups per CU that deals the tiles in
- * the same order.  Every form gives the same gradients bit for bit.
+ * load balancing).  Causal passes of more than 2 tiles per CU and either at
+ * most 8 per CU, or at most 32 tiles per sequence with rounds of the CUs' work-
+ * group slots times tiles per sequence at most 256, run on a persistent grid of
+ * two work-groups per CU that deals the tiles in the same order.  Every form
+ * gives the same gradients bit for bit.
  */
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
            const float* lse, void* dq, void* dk, void* dv, void* workspace,

@@ -109,22 +109,28 @@ int fwd_slots(int* slots) {
     return FA_OK;
 }
 
-// Grid of a backward pass with `items` work items: one work-group per item, or,
-// for dense causal passes of more than one and at most four rounds of the
+// Grid of a backward pass with `items` work items (`n_tiles` per sequence): one
+// work-group per item, or, for dense causal passes of more than one round of the
 // work-group slots, a persistent grid of one work-group per slot (rounded down
-// to a multiple of 8) that deals the items itself.  Measured on MI355X
-// (alternating, bitwise the same gradients): B8 H16 N2048 d128 causal dK/dV
-// 0.293 against 0.323 ms and dQ 0.236 against 0.262 ms, B4 H16 N4096 5% and 4%
-// faster; at eight rounds (B8 H16 N4096) 0.5-1% slower, on the long context
-// (B1 H16 N32768) 4% slower, non-causal 3-4% slower.
+// to a multiple of 8) that deals the items itself in the same order, when the
+// pass has at most four rounds, or at most 32 tiles per sequence with rounds
+// times tiles per sequence at most 256 (eight rounds of 32 tiles, sixteen of
+// 16).  Measured on MI355X (fa_bwd, alternating, bitwise the same gradients):
+// faster at B8 H16 N2048 d128 (506 against 522-550 us), B4 H16 N4096 (3%), B8
+// H16 N4096 (the headline, 0.5-2% on two boxes), B8 H16 N4096 d64 (2-2.5%), B32
+// H16 N2048 (2%), B64 H16 N1024 d64 (6.5%); slower at B16 H16 N4096 (0.5%, 16
+// rounds of 32 tiles), B2 H32 N8192 (0.7%, 64 tiles), B1 H16 N32768 (3.3%, 256
+// tiles) and non-causal (3-4%), which keep one work-group per item.
 template <bool VARLEN>
-int bwd_grid(int64_t items, int causal, int* grid) {
+int bwd_grid(int64_t items, int n_tiles, int causal, int* grid) {
     int slots = 0;
     const int st = fwd_slots(&slots);
     if (st) return st;
     if (items > INT_MAX) return FA_ERR_SHAPE;
     *grid = (int)items;
-    if (!VARLEN && causal && items > slots && items <= 4 * (int64_t)slots) *grid = slots / 8 * 8;
+    if (!VARLEN && causal && items > slots &&
+        (items <= 4 * (int64_t)slots || (n_tiles <= 32 && items * n_tiles <= 256 * (int64_t)slots)))
+        *grid = slots / 8 * 8;
     return FA_OK;
 }
 
@@ -141,7 +147,7 @@ int launch_bwd_dkdv_d(AttnParams p, int causal, hipStream_t s) {
     using KV = BwdKVCfg<D>;
     p.n_tiles = (p.nk + KV::BN - 1) / KV::BN;
     int grid = 0;
-    const int st = bwd_grid<VARLEN>((int64_t)p.n_tiles * p.H * p.batch, causal, &grid);
+    const int st = bwd_grid<VARLEN>((int64_t)p.n_tiles * p.H * p.batch, p.n_tiles, causal, &grid);
     if (st) return st;
     if (!VARLEN && grid < p.n_tiles * p.H * p.batch) return launch(fa_bwd_dkdv_persistent_kernel<D>, grid, KV::NW * 64, s, p);
     return causal ? launch(fa_bwd_dkdv_kernel<D, true, VARLEN>, grid, KV::NW * 64, s, p)
@@ -153,7 +159,7 @@ int launch_bwd_dq_d(AttnParams p, int causal, hipStream_t s) {
     using Q = BwdQCfg<D>;
     p.n_tiles = (p.nq + Q::BM - 1) / Q::BM;
     int grid = 0;
-    const int st = bwd_grid<VARLEN>((int64_t)p.n_tiles * p.H * p.batch, causal, &grid);
+    const int st = bwd_grid<VARLEN>((int64_t)p.n_tiles * p.H * p.batch, p.n_tiles, causal, &grid);
     if (st) return st;
     if (!VARLEN && grid < p.n_tiles * p.H * p.batch) return launch(fa_bwd_dq_persistent_kernel<D, DOT>, grid, Q::NW * 64, s, p);
     return causal ? launch(fa_bwd_dq_kernel<D, true, VARLEN, DOT>, grid, Q::NW * 64, s, p)

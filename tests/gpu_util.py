@@ -109,13 +109,16 @@ def bwd_is_fused(B, H, Nq, Nk, causal) -> bool:
 def bwd_is_persistent(B, H, Nq, Nk, causal) -> bool:
     """Whether fa_bwd runs its dK/dV (128-key tiles) and dQ (128-row tiles) passes
     on persistent grids: dense causal backwards that do not take the one-launch
-    form, for each pass that has more work items than two per CU and at most
-    eight (returns the dK/dV pass's answer, then the dQ pass's)."""
+    form, for each pass that has more work items than two per CU and either at
+    most eight per CU, or at most 32 tiles per sequence with items times tiles
+    per sequence at most 512 per CU (returns the dK/dV pass's answer, then the
+    dQ pass's)."""
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     if not causal or bwd_is_fused(B, H, Nq, Nk, causal):
         return False, False
-    items = (-(-Nk // 128) * B * H, -(-Nq // 128) * B * H)
-    return tuple(2 * cus < n <= 8 * cus for n in items)
+    tiles = (-(-Nk // 128), -(-Nq // 128))
+    return tuple(2 * cus < t * B * H and (t * B * H <= 8 * cus or (t <= 32 and t * t * B * H <= 512 * cus))
+                 for t in tiles)
 
 
 def run_dense(x, scale, causal, backward=True):

@@ -1,16 +1,17 @@
 """The persistent backward grids on the GPU.
 
 For dense causal backwards that do not take the one-launch form, a pass
-(dK/dV over 128-key tiles, dQ over 128-row tiles) with more than two and at
-most eight work items per CU runs on a persistent grid of two work-groups per
-CU that deals the items in the per-tile grid's order.  Each item is the same
+(dK/dV over 128-key tiles, dQ over 128-row tiles) with more than two work items
+per CU and either at most eight per CU or at most 32 tiles per sequence runs on
+a persistent grid of two work-groups per CU that deals the items in the
+per-tile grid's order.  Each item is the same
 arithmetic as in the per-tile kernels, which the varlen entry point always
 runs; on equal-length sequences, packed, with the dense forward's O and LSE,
 it must give the same gradients bit for bit.  Sampled (batch entry, head)
-pairs are also compared with the oracle.  Cases: the largest and smallest
-grids of the path at d = 128 and d = 64 on a 256-CU MI355X, and a ragged one
-(N not a multiple of 128, head and batch counts not multiples of 8, three
-rounds of the grid).
+pairs are also compared with the oracle.  Cases: the headline shape (eight
+rounds), the largest and smallest grids of the four-round range at d = 128 and
+d = 64 on a 256-CU MI355X, and ragged ones (N not a multiple of 128, head and
+batch counts not multiples of 8, three rounds of the grid).
 """
 
 import pytest
@@ -24,6 +25,7 @@ pytestmark = pytest.mark.gpu
 
 CASES = [
     # B, N, H, d
+    (8, 4096, 16, 128),   # the headline shape: 4096 items per pass, eight rounds
     (8, 2048, 16, 128),   # 2048 items per pass: four rounds
     (4, 4096, 16, 128),
     (5, 2500, 13, 128),   # 1300 items per pass, ragged
