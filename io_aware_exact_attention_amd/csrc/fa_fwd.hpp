@@ -107,7 +107,7 @@ __device__ __forceinline__ void fwd_tile(const AttnParams& p, char* smem, int bh
     static_assert(SPLIT == 1 || SPLIT == 2, "one or two key halves");
     static_assert(!CARRY || (SPLIT == 1 && !VARLEN), "carried items: dense, one key range");
     static_assert(!CARRY || kCarrySliceOff<D> + C::NW * 32 * 2 * D <= kCarryLdsBytes<D>, "slices fit");
-    // (wave-uniform: scalar branches, which the compiler's wait bookkeeping follows)
+    // (wave-uniform, so that its branches are scalar ones)
     const bool pre = CARRY && __builtin_amdgcn_readfirstlane((int)nx.pre) != 0;
     // (carried items run in a loop: opaque to the optimiser, so that offsets
     // derived from the lane are recomputed per item instead of held across items)
@@ -202,7 +202,7 @@ __device__ __forceinline__ void fwd_tile(const AttnParams& p, char* smem, int bh
             loader.load(ldsb + C::TILE_BYTES, vbase, kv_bytes, 0, wave_s);
         }
         if (n_kv > 1) loader.load(ldsb + 2 * C::TILE_BYTES, kbase, kv_bytes, C::BN * row_bytes, wave_s);
-        wait_vmem();
+        if constexpr (CARRY) wait_vmem();   // (before this wave reads its Q rows)
     } else {
         // (a carried item: its loads were issued before the previous item's
         // kCarryStores<D> stores, which may stay in flight)
@@ -306,6 +306,7 @@ __device__ __forceinline__ void fwd_tile(const AttnParams& p, char* smem, int bh
     };
 
     f32x16 s[C::KB];   // scores of the tile the loop is at
+    if constexpr (!CARRY) wait_vmem();
     __syncthreads();
     if (n_w > 0) {
         scores(ldsb, s);
