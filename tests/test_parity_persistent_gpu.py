@@ -43,3 +43,41 @@ def test_persistent_equals_fa_fwd(case):
     if B * N * Nk * H <= 2 * 300 * 300 * 8 or gu.fwd_is_key_split(B, H, N, causal):
         o_ref, l_ref = oracle.attention_forward(x["q"], x["k"], x["v"], scale, causal)
         gu.check_forward(o2, l2, o_ref, l_ref, f"persistent {case}")
+
+
+CARRY_CASES = [
+    # B, N, H: causal d = 128 grids of several rounds with at most 32 tiles per
+    # sequence, which fa_fwd runs on the persistent kernel with carried items
+    (4, 2048, 16),    # two rounds
+    (8, 4096, 16),    # the headline shape: eight rounds
+    (3, 4000, 16),    # ragged tail, three rounds
+    (5, 2500, 13),    # ragged, 65 pairs (not a multiple of 8)
+]
+
+
+@pytest.mark.parametrize("case", CARRY_CASES, ids=lambda c: "B{}_N{}_H{}".format(*c))
+def test_carried_items_equal_per_tile_kernel(case):
+    """The persistent forward's carried items (each item issues its successor's
+    first K/V tiles and Q rows before its own stores) compute each tile exactly
+    as the per-tile kernel does, which the varlen entry point always runs: on
+    equal-length sequences, packed, O and LSE must be equal bit for bit; two
+    sampled (batch, head) slices are also compared with the oracle."""
+    gu.need_gpu()
+    B, N, H = case
+    d = 128
+    if gu.fwd_is_key_split(B, H, N, True):
+        pytest.skip("this device runs the key-split kernel for this grid")
+    gu.announce(f"carried forward {case}")
+    x = wl.make_dense(B, N, H, d, seed=4500 + N + H, with_dout=False)
+    q, k, v = (x[n].cuda() for n in ("q", "k", "v"))
+    scale = d ** -0.5
+    o1, l1 = fa355.attention_forward(q, k, v, scale, True)
+    cu = (torch.arange(B + 1, dtype=torch.int32) * N).cuda()
+    pk = lambda t: t.reshape(B * N, H, d)
+    o2, l2 = fa355.attention_forward_varlen(pk(q), pk(k), pk(v), cu, cu, N, N, scale, True)
+    torch.cuda.synchronize()
+    assert torch.equal(pk(o1), o2) and torch.equal(l1, l2)
+    for b, h in ((0, 0), (B - 1, H - 1)):
+        xs = {n: x[n][b:b + 1, :, h:h + 1] for n in ("q", "k", "v")}
+        o_ref, l_ref = oracle.attention_forward(xs["q"], xs["k"], xs["v"], scale, True)
+        gu.check_forward(o1[b:b + 1, :, h:h + 1], l1[b:b + 1, h:h + 1], o_ref, l_ref, f"carried {case} b{b} h{h}")
