@@ -550,7 +550,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(heads and batch entries are independent, see the design notes)", file=sys.stderr)
+              "(the path would shard by batch entry and head, which need no communication)", file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
