@@ -35,3 +35,32 @@ def test_o_tolerance_and_output_floor():
     # a floor-limited entry does not excuse another entry's error
     with pytest.raises(AssertionError):
         _fwd([4.0, 1.02], [4.0105, 1.0])
+
+
+class _Props:
+    multi_processor_count = 256
+
+
+@pytest.mark.parametrize("cus", [256, 304, 80])
+def test_kernel_choice_mirrors_agree(monkeypatch, cus):
+    """bench.py and the GPU tests each restate fa_fwd's and fa_bwd's documented
+    kernel choices; both restatements must give the same answer on every shape
+    (CPU: the device's CU count is stubbed)."""
+    import bench
+
+    props = _Props()
+    props.multi_processor_count = cus
+    monkeypatch.setattr(torch.cuda, "get_device_properties", lambda *_: props)
+    for B in (1, 2, 3, 4, 8, 16, 32, 64):
+        for H in (1, 8, 13, 16, 32):
+            for N in (1, 127, 128, 1000, 1024, 2048, 2500, 4096, 8192, 32768):
+                for causal in (False, True):
+                    fused = bench.fa_bwd_is_fused(B, H, N, causal)
+                    assert fused == gu.bwd_is_fused(B, H, N, N, causal)
+                    pers = gu.bwd_is_persistent(B, H, N, N, causal)
+                    names = bench.fa_bwd_pass_kernel_names(B, H, N, causal)
+                    if not fused:
+                        assert (names[1] == "fa_bwd_dkdv_persistent_kernel") == pers[0]
+                        assert (names[0] == "fa_bwd_dq_persistent_kernel") == pers[1]
+                    split = bench.fa_fwd_kernel_name(B, H, N, causal) == "fa_fwd_split_kernel"
+                    assert split == gu.fwd_is_key_split(B, H, N, causal)
