@@ -5,15 +5,6 @@
 
 namespace fa355 {
 
-// LDS tiles are row-major [row][D] bf16 with the 16-byte chunks of each row
-// permuted: logical chunk c of row r sits at physical chunk c ^ tile_swz(r).
-// Measured on gfx950 (bank-conflict counter), the LDS serves a ds_read_b128 in
-// groups of 16 lanes and a ds_read_b64_tr_b16 in groups of 32 lanes, each group
-// conflict-free when it touches 256 distinct bytes modulo 256.  The kernels read
-// (a) 16 consecutive rows at one logical chunk (row-wise operands) and (b) 4
-// consecutive rows (from a multiple of 4) at 4 adjacent chunks, 64 bytes each
-// (transposed operands).  The XOR below makes (a) a permutation of the 16 chunk
-// slots and sends the 4 rows of (b) to 4 different 64-byte bank groups.
 // Direct HBM->LDS loads issued as inline assembly, so that the compiler does not
 // see them.  The compiler cannot tell which LDS bytes a direct-to-LDS load
 // writes, so for the ones it sees it makes LDS reads wait for all of them
@@ -56,6 +47,16 @@ __device__ __forceinline__ void dma_lds4(const u32x4& rsrc, FA_LDS void* lds, in
         : "memory");
 }
 
+
+// LDS tiles are row-major [row][D] bf16 with the 16-byte chunks of each row
+// permuted: logical chunk c of row r sits at physical chunk c ^ tile_swz(r).
+// Measured on gfx950 (bank-conflict counter), the LDS serves a ds_read_b128 in
+// groups of 16 lanes and a ds_read_b64_tr_b16 in groups of 32 lanes, each group
+// conflict-free when it touches 256 distinct bytes modulo 256.  The kernels read
+// (a) 16 consecutive rows at one logical chunk (row-wise operands) and (b) 4
+// consecutive rows (from a multiple of 4) at 4 adjacent chunks, 64 bytes each
+// (transposed operands).  The XOR below makes (a) a permutation of the 16 chunk
+// slots and sends the 4 rows of (b) to 4 different 64-byte bank groups.
 template <int D>
 __device__ __forceinline__ int tile_swz(int row) {
     if constexpr (D == 128) return 4 * (row & 3) + ((row >> 2) & 3);
