@@ -491,10 +491,10 @@ def fa_bwd_pass_kernel_names(B: int, H: int, N: int, causal: bool) -> tuple:
 
 def fa_bwd_is_fused(B: int, H: int, N: int, causal: bool) -> bool:
     """Whether fa_bwd runs as the row-dot kernel and one launch holding both
-    passes (its documented choice for small dense grids: at most 8 causal or 2
+    passes (its documented choice for small dense grids: at most 6 causal or 2
     non-causal dK/dV plus dQ work items of 128 rows per CU)."""
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    return 2 * (-(-N // 128)) * B * H <= (8 if causal else 2) * cus
+    return 2 * (-(-N // 128)) * B * H <= (6 if causal else 2) * cus
 
 
 def small_config_rates(name: str, causal: bool, steps: int = 50, warmup: int = 10) -> dict:

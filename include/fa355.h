@@ -133,7 +133,7 @@ size_t fa_bwd_workspace_bytes(int batch_or_nseq, int H, int nq, int d);
  * (fully overwritten).  workspace: device buffer of at least
  * fa_bwd_workspace_bytes(B,H,Nq,d) bytes, 4-byte aligned; its contents on entry
  * do not matter and on return are unspecified.
- * Kernels: fa_bwd_dq_dot's then fa_bwd_dkdv's; for small grids (at most 8
+ * Kernels: fa_bwd_dq_dot's then fa_bwd_dkdv's; for small grids (at most 6
  * causal or 2 non-causal dK/dV plus dQ tiles of 128 rows per CU) fa_bwd_dot's
  * kernel, then one launch holding both passes' tiles, so that each pass's causal
  * tail overlaps the other's work ("LLM Systems 22: Flash Attention", §4.1.5

@@ -180,14 +180,15 @@ int launch_bwd_fused_d(AttnParams p, int causal, hipStream_t s) {
 // Dense backwards whose dK/dV and dQ work items (128-row tiles) together number
 // at most this many per CU run both passes in one launch (fa_bwd_fused_kernel,
 // after the row-dot kernel).  Measured on MI355X (fa_bwd, both forms bitwise
-// equal): causal, 12-27% faster from 1 to 4 items per CU and 10-15% at 8, equal
-// at 16, and 11-15% slower at 32 or more, where the longest-first order over all
-// heads loses the per-head L2 sharing of the two separate kernels; non-causal
-// (every tile equally long), 8% faster at 2 items per CU but 12% slower at 4,
-// where the separate kernels' single rounds are already balanced and the
-// separate row-dot kernel costs more than the merged tails save.
+// equal): causal, against two per-tile kernels 12-27% faster from 1 to 4 items
+// per CU, and against the two persistent kernels (which take the passes of more
+// than one round of slots) 18% faster at 5 items per CU (B5 H16 N1024 d128) and
+// 5-6% at 6, but equal to 6% slower at 7 and 8-12% slower at 8 (B8 H16 N1024 d64
+// and d128); non-causal (every tile equally long), 8% faster at 2 items per CU
+// but 12% slower at 4, where the separate kernels' single rounds are already
+// balanced and the separate row-dot kernel costs more than the merged tails save.
 #ifndef FA355_FUSED_BWD_CAUSAL_ITEMS_PER_CU
-#define FA355_FUSED_BWD_CAUSAL_ITEMS_PER_CU 8
+#define FA355_FUSED_BWD_CAUSAL_ITEMS_PER_CU 6
 #endif
 #ifndef FA355_FUSED_BWD_FULL_ITEMS_PER_CU
 #define FA355_FUSED_BWD_FULL_ITEMS_PER_CU 2

@@ -100,10 +100,10 @@ def fwd_is_key_split(B, H, Nq, causal) -> bool:
 
 def bwd_is_fused(B, H, Nq, Nk, causal) -> bool:
     """Whether fa_bwd runs the row-dot kernel and then both passes in one launch:
-    dense grids of at most 8 (causal) or 2 (non-causal) dK/dV plus dQ work items
+    dense grids of at most 6 (causal) or 2 (non-causal) dK/dV plus dQ work items
     (128-row tiles) per CU."""
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    return (-(-Nk // 128) + -(-Nq // 128)) * B * H <= (8 if causal else 2) * cus
+    return (-(-Nk // 128) + -(-Nq // 128)) * B * H <= (6 if causal else 2) * cus
 
 
 def bwd_is_persistent(B, H, Nq, Nk, causal) -> bool:

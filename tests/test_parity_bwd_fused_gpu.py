@@ -1,6 +1,6 @@
 """The one-launch backward of small dense grids on the GPU.
 
-fa_bwd runs grids of at most 8 (causal) or 2 (non-causal) dK/dV plus dQ work
+fa_bwd runs grids of at most 6 (causal) or 2 (non-causal) dK/dV plus dQ work
 items per CU as the row-dot kernel followed by one launch that holds both passes'
 work items.  Each work
 item is the same computation as in the two-kernel backward (the row-dot kernel
@@ -9,7 +9,7 @@ row-dot), so the gradients must equal the stage entry points' (fa_bwd_dq_dot,
 then fa_bwd_dkdv) bit for bit; they are also compared with the oracle.  Cases
 cover both masks, Nq != Nk in both directions (more dQ than dK/dV items and the
 reverse), ragged tails, head and batch counts that are not multiples of 8, and
-the largest grids that take this path on a 256-CU MI355X (causal B8 H16 N1024,
+the largest grids that take this path on a 256-CU MI355X (causal B6 H16 N1024,
 non-causal B2 H16 N1024).
 """
 
@@ -31,7 +31,7 @@ CASES = [
     (1, 2048, 2048, 8, 128, True),
     (2, 1024, 1024, 16, 64, False),  # the largest non-causal grid on this path
     (4, 1024, 1024, 16, 64, True),
-    (8, 1024, 1024, 16, 64, True),   # the largest causal grid on this path
+    (6, 1024, 1024, 16, 64, True),   # the largest causal grid on this path
 ]
 
 
